@@ -1,0 +1,211 @@
+"""ctypes binding of the C ABI in include/mk.h.
+
+Argument marshalling only: every step of the decode runs in the HIP kernel of
+libmk.so.  If the library is missing this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK = 0
+STATUS_BAD_TOKEN = 1
+STATUS_BAD_POSITION = 2
+STATUS_BAD_SEQLEN = 4
+STATUS_TIMEOUT = 8
+ERRORS = {-1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_OOM", -4: "MK_ERR_HIP",
+          -5: "MK_ERR_PLAN"}
+
+
+class MKError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {ERRORS.get(code, code)}")
+        self.code = code
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("tied_embeddings", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
+                ("max_seq", ctypes.c_int32)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class WeightPtrs(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("attn_norm", _PP), ("q_proj", _PP), ("k_proj", _PP), ("v_proj", _PP), ("o_proj", _PP),
+                ("q_norm", _PP), ("k_norm", _PP), ("mlp_norm", _PP), ("gate_proj", _PP), ("up_proj", _PP),
+                ("down_proj", _PP)]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("batch_cap", ctypes.c_int32),
+                ("seq_cap", ctypes.c_int32)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [("n_tasks", ctypes.c_int32), ("max_tasks_per_cu", ctypes.c_int32),
+                ("n_counters", ctypes.c_int32), ("mfma", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
+                ("max_cu_weight_bytes", ctypes.c_int64), ("stage_balance_min", ctypes.c_double),
+                ("stage_tasks", ctypes.c_int32 * 6), ("stage_ksplit", ctypes.c_int32 * 6),
+                ("stage_rows_per_task", ctypes.c_int32 * 6)]
+
+
+EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_get_status", "mk_reset",
+           "mk_destroy", "mk_error_string", "mk_plan"]
+STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m decode_megakernel_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    L.mk_create.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(WeightPtrs), ctypes.POINTER(vp)]
+    L.mk_decode_step.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp]
+    L.mk_copy_hidden.argtypes = [vp, i32, vp, vp]
+    L.mk_copy_state.argtypes = [vp, i32, i32, vp, vp]
+    L.mk_get_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+    L.mk_reset.argtypes = [vp, vp]
+    L.mk_destroy.argtypes = [vp]
+    L.mk_error_string.argtypes = [ctypes.c_int]
+    L.mk_error_string.restype = ctypes.c_char_p
+    L.mk_plan.argtypes = [ctypes.POINTER(ModelCfg), i32, i32, ctypes.POINTER(PlanStats)]
+    for name in EXPORTS:
+        if name != "mk_error_string":
+            getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str):
+    if rc != MK_OK:
+        raise MKError(rc, what)
+
+
+def model_cfg(shape, max_batch: int, max_seq: int) -> ModelCfg:
+    return ModelCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                    shape.intermediate, shape.vocab, int(shape.tied_embeddings), int(shape.qk_norm),
+                    float(shape.rope_theta), float(shape.rms_eps), int(max_batch), int(max_seq))
+
+
+def plan(shape, batch: int, n_cu: int = 256, max_batch: int = 16, max_seq: int = 8192) -> dict:
+    """Build and validate the per-CU schedule on the host (no GPU)."""
+    st = PlanStats()
+    cfg = model_cfg(shape, max_batch, max_seq)
+    _check(lib().mk_plan(ctypes.byref(cfg), int(batch), int(n_cu), ctypes.byref(st)), "mk_plan")
+    out = {k: getattr(st, k) for k, _ in PlanStats._fields_}
+    for k in ("stage_tasks", "stage_ksplit", "stage_rows_per_task"):
+        out[k] = list(out[k])
+    return out
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class DecodeEngine:
+    """Owns one mk_handle; the caller owns weights, KV cache and step buffers.
+
+    `weights` maps Hugging Face names to contiguous bf16 CUDA tensors.
+    """
+
+    def __init__(self, shape, weights: dict, max_batch: int, max_seq: int):
+        self.shape = shape
+        self._keep = []   # ctypes arrays that the C side reads during mk_create
+        L = shape.n_layers
+
+        def ptr(name):
+            t = weights[name]
+            assert t.is_cuda and t.is_contiguous(), name
+            return t.data_ptr()
+
+        def arr(suffix, optional=False):
+            if optional and not shape.qk_norm:
+                return ctypes.cast(None, _PP)
+            a = (ctypes.c_void_p * L)(*[ptr(f"model.layers.{l}.{suffix}") for l in range(L)])
+            self._keep.append(a)
+            return ctypes.cast(a, _PP)
+
+        wp = WeightPtrs(
+            ptr("model.embed_tokens.weight"),
+            None if shape.tied_embeddings else ptr("lm_head.weight"),
+            ptr("model.norm.weight"),
+            arr("input_layernorm.weight"), arr("self_attn.q_proj.weight"), arr("self_attn.k_proj.weight"),
+            arr("self_attn.v_proj.weight"), arr("self_attn.o_proj.weight"),
+            arr("self_attn.q_norm.weight", True), arr("self_attn.k_norm.weight", True),
+            arr("post_attention_layernorm.weight"), arr("mlp.gate_proj.weight"), arr("mlp.up_proj.weight"),
+            arr("mlp.down_proj.weight"))
+        self.cfg = model_cfg(shape, max_batch, max_seq)
+        h = ctypes.c_void_p()
+        _check(lib().mk_create(ctypes.byref(self.cfg), ctypes.byref(wp), ctypes.byref(h)), "mk_create")
+        self.handle = h
+        self.max_batch = max_batch
+
+    def step(self, tokens, positions, seq_lens, k_cache, v_cache, logits, next_tokens=None, stream=None,
+             batch=None):
+        """Enqueue one decode step; all tensors are CUDA tensors the caller owns.
+
+        k_cache, v_cache: bf16 [L][batch_cap][n_kv][seq_cap][hd]; tokens, positions,
+        seq_lens: int32 [>= batch]; logits: float32 [>= batch, vocab]."""
+        b = int(tokens.numel()) if batch is None else int(batch)
+        kv = KVCache(k_cache.data_ptr(), v_cache.data_ptr(), int(k_cache.shape[1]), int(k_cache.shape[3]))
+        rc = lib().mk_decode_step(self.handle, b, tokens.data_ptr(), positions.data_ptr(), seq_lens.data_ptr(),
+                                  ctypes.byref(kv), logits.data_ptr(),
+                                  None if next_tokens is None else next_tokens.data_ptr(),
+                                  _stream_handle(stream))
+        _check(rc, "mk_decode_step")
+
+    def copy_hidden(self, batch: int, out, stream=None):
+        _check(lib().mk_copy_hidden(self.handle, int(batch), out.data_ptr(), _stream_handle(stream)),
+               "mk_copy_hidden")
+
+    def copy_state(self, which: int, batch: int, out, stream=None):
+        _check(lib().mk_copy_state(self.handle, int(which), int(batch), out.data_ptr(), _stream_handle(stream)),
+               "mk_copy_state")
+
+    def state(self, which: int, batch: int):
+        """Mid-state buffer of the last step as a new CUDA tensor [layers, batch, width]."""
+        import torch
+        sh = self.shape
+        L = sh.n_layers
+        spec = {STATE_HIDDEN: (L + 1, sh.hidden, torch.float32), STATE_HMID: (L, sh.hidden, torch.float32),
+                STATE_QKV: (L, sh.q_dim + 2 * sh.kv_dim, torch.float32),
+                STATE_ATTN: (L, sh.q_dim, torch.bfloat16), STATE_ACT: (L, sh.intermediate, torch.bfloat16)}
+        nl, width, dt = spec[which]
+        out = torch.empty((nl, batch, width), dtype=dt, device="cuda")
+        self.copy_state(which, batch, out)
+        return out
+
+    def status(self, stream=None) -> int:
+        s = ctypes.c_uint32()
+        _check(lib().mk_get_status(self.handle, _stream_handle(stream), ctypes.byref(s)), "mk_get_status")
+        return int(s.value)
+
+    def reset(self, stream=None):
+        _check(lib().mk_reset(self.handle, _stream_handle(stream)), "mk_reset")
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().mk_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

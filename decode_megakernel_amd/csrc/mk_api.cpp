@@ -1,0 +1,462 @@
+// C ABI of the decode-step megakernel: argument checks, workspace, schedule
+// cache and the single launch per step.  See include/mk.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <new>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+
+namespace mk {
+hipError_t launch_step(const DevArgs& A, hipStream_t stream);
+size_t lds_bytes(int nslot, int xb_bytes);
+}  // namespace mk
+
+using namespace mk;
+
+namespace {
+
+struct GraphDev {
+  Plan plan;
+  Task* d_tasks = nullptr;
+  int* d_off = nullptr;
+  int* d_expect = nullptr;
+  float* d_part = nullptr;
+  uint32_t* d_grp = nullptr;
+};
+
+int env_int(const char* name, int def) {
+  const char* v = getenv(name);
+  if (!v || !*v) return def;
+  return atoi(v);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct mk_handle {
+  mk_model_cfg cfg;
+  int device = 0;
+  int ncu = 0;
+  int nslot = 6;
+  int xb = 0;
+  int mfma_min_batch = 8;
+  uint64_t timeout_ticks = 0;
+  LayerW* d_layers = nullptr;
+  const uint16_t* embed = nullptr;
+  const uint16_t* lm_head = nullptr;
+  const uint16_t* final_norm = nullptr;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  // workspace views
+  float *hres, *hmid, *ssattn, *ssmlp, *qkv, *apart, *rope;
+  uint16_t *xattn, *xmlp, *attn_out, *act;
+  uint32_t *banks, *seg_ctr, *status;
+  int ctr_stride = 0, bank_words = 0;
+  std::map<int, GraphDev> graphs;
+  uint64_t step = 0;
+};
+
+extern "C" {
+
+const char* mk_error_string(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_ERR_INVALID_ARG: return "invalid argument";
+    case MK_ERR_UNSUPPORTED: return "unsupported model shape";
+    case MK_ERR_OOM: return "device out of memory";
+    case MK_ERR_HIP: return "HIP runtime error";
+    case MK_ERR_PLAN: return "schedule validation failed";
+  }
+  return "unknown error";
+}
+
+static int check_cfg(const mk_model_cfg* c) {
+  if (!c) return MK_ERR_INVALID_ARG;
+  if (c->n_layers < 1 || c->hidden < 64 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->intermediate < 64 ||
+      c->vocab < 1 || c->max_batch < 1 || c->max_batch > kMaxBatch || c->max_seq < 1 || !(c->rms_eps > 0.f) ||
+      !(c->rope_theta > 0.0))
+    return MK_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads) return MK_ERR_INVALID_ARG;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (c->head_dim != 64 && c->head_dim != 128) return MK_ERR_UNSUPPORTED;
+  if (G > (c->head_dim == 128 ? 4 : 8)) return MK_ERR_UNSUPPORTED;
+  if (c->hidden % 64 || c->intermediate % 64) return MK_ERR_UNSUPPORTED;
+  // a K slice of one row of 16 bf16 columns per sequence must fit the staging buffer
+  return MK_OK;
+}
+
+static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
+  PlanCfg p;
+  p.L = c->n_layers;
+  p.d = c->hidden;
+  p.nq = c->n_q_heads;
+  p.nkv = c->n_kv_heads;
+  p.hd = c->head_dim;
+  p.I = c->intermediate;
+  p.V = c->vocab;
+  p.ncu = ncu;
+  p.xb_bytes = xb;
+  p.mfma_min_batch = mfma_min;
+  return p;
+}
+
+static int xb_for(int lds_max, int nslot) {
+  long long xb = (long long)lds_max - (long long)nslot * kChunkBytes - kRedBytes - 512;
+  xb &= ~255LL;
+  return (int)xb;
+}
+
+int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats* out) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!out || n_cu < 1 || batch < 1 || batch > cfg->max_batch) return MK_ERR_INVALID_ARG;
+  const int nslot = env_int("MK_NSLOT", 6);
+  PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot), env_int("MK_MFMA_MIN_BATCH", 8));
+  Plan P;
+  rc = build_plan(pc, batch, &P);
+  if (rc) return rc;
+  memset(out, 0, sizeof(*out));
+  out->n_tasks = P.n_tasks;
+  out->max_tasks_per_cu = P.max_tasks_per_cu;
+  out->n_counters = P.n_counters;
+  out->mfma = P.mfma;
+  out->weight_bytes = P.weight_bytes;
+  out->max_cu_weight_bytes = P.max_cu_weight_bytes;
+  out->stage_balance_min = P.balance_min;
+  for (int i = 0; i < 6; ++i) {
+    out->stage_tasks[i] = P.stage_tasks[i];
+    out->stage_ksplit[i] = P.stage_ksplit[i];
+    out->stage_rows_per_task[i] = P.stage_rows[i];
+  }
+  free_plan(&P);
+  return MK_OK;
+}
+
+int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!w || !out) return MK_ERR_INVALID_ARG;
+  const int L = cfg->n_layers;
+  if (!w->embed || !w->final_norm || (!cfg->tied_embeddings && !w->lm_head) || !w->attn_norm || !w->q_proj ||
+      !w->k_proj || !w->v_proj || !w->o_proj || !w->mlp_norm || !w->gate_proj || !w->up_proj || !w->down_proj)
+    return MK_ERR_INVALID_ARG;
+  if (cfg->qk_norm && (!w->q_norm || !w->k_norm)) return MK_ERR_INVALID_ARG;
+  for (int l = 0; l < L; ++l) {
+    if (!w->attn_norm[l] || !w->q_proj[l] || !w->k_proj[l] || !w->v_proj[l] || !w->o_proj[l] || !w->mlp_norm[l] ||
+        !w->gate_proj[l] || !w->up_proj[l] || !w->down_proj[l])
+      return MK_ERR_INVALID_ARG;
+    if (cfg->qk_norm && (!w->q_norm[l] || !w->k_norm[l])) return MK_ERR_INVALID_ARG;
+  }
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return MK_ERR_OOM;
+  h->cfg = *cfg;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return MK_ERR_HIP;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) {
+    delete h;
+    return MK_ERR_HIP;
+  }
+  h->ncu = env_int("MK_NUM_CU", prop.multiProcessorCount);
+  if (h->ncu < 1 || h->ncu > prop.multiProcessorCount) h->ncu = prop.multiProcessorCount;
+  h->nslot = env_int("MK_NSLOT", 6);
+  if (h->nslot < kComputeWaves) h->nslot = kComputeWaves;
+  if (h->nslot > kMaxSlots) h->nslot = kMaxSlots;
+  h->xb = xb_for((int)prop.sharedMemPerBlock, h->nslot);
+  if (h->xb < 4096) {
+    delete h;
+    return MK_ERR_UNSUPPORTED;
+  }
+  h->mfma_min_batch = env_int("MK_MFMA_MIN_BATCH", 8);
+  h->timeout_ticks = (uint64_t)env_int("MK_SPIN_TIMEOUT_MS", 2000) * 100000ull;
+
+  const int d = cfg->hidden, bc = cfg->max_batch, hd = cfg->head_dim, nkv = cfg->n_kv_heads;
+  const int qdim = cfg->n_q_heads * hd, nqkv = qdim + 2 * nkv * hd, I = cfg->intermediate;
+  h->ctr_stride = ctr_stride(L);
+  h->bank_words = kShards * h->ctr_stride + 2 * kMaxBatch;
+  // workspace layout
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  size_t o_hres = take((size_t)(L + 1) * bc * d * 4);
+  size_t o_hmid = take((size_t)L * bc * d * 4);
+  size_t o_xattn = take((size_t)(L + 1) * bc * d * 2);
+  size_t o_xmlp = take((size_t)L * bc * d * 2);
+  size_t o_ssattn = take((size_t)(L + 1) * (d / 16) * bc * 4);
+  size_t o_ssmlp = take((size_t)L * (d / 16) * bc * 4);
+  size_t o_qkv = take((size_t)L * bc * nqkv * 4);
+  size_t o_aout = take((size_t)L * bc * qdim * 2);
+  size_t o_act = take((size_t)L * bc * I * 2);
+  size_t o_apart = take((size_t)(h->ncu + bc * nkv) * kApartGroup * (hd + 4) * 4);
+  size_t o_banks = take((size_t)2 * h->bank_words * 4);
+  size_t o_seg = take((size_t)bc * nkv * 4);
+  size_t o_status = take(64);
+  size_t o_rope = take((size_t)cfg->max_seq * (hd / 2) * 2 * 4);
+  h->ws_bytes = off;
+  if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
+    delete h;
+    return MK_ERR_OOM;
+  }
+  if (hipMemset(h->ws, 0, h->ws_bytes) != hipSuccess) {
+    hipFree(h->ws);
+    delete h;
+    return MK_ERR_HIP;
+  }
+  h->hres = (float*)(h->ws + o_hres);
+  h->hmid = (float*)(h->ws + o_hmid);
+  h->xattn = (uint16_t*)(h->ws + o_xattn);
+  h->xmlp = (uint16_t*)(h->ws + o_xmlp);
+  h->ssattn = (float*)(h->ws + o_ssattn);
+  h->ssmlp = (float*)(h->ws + o_ssmlp);
+  h->qkv = (float*)(h->ws + o_qkv);
+  h->attn_out = (uint16_t*)(h->ws + o_aout);
+  h->act = (uint16_t*)(h->ws + o_act);
+  h->apart = (float*)(h->ws + o_apart);
+  h->banks = (uint32_t*)(h->ws + o_banks);
+  h->seg_ctr = (uint32_t*)(h->ws + o_seg);
+  h->status = (uint32_t*)(h->ws + o_status);
+  h->rope = (float*)(h->ws + o_rope);
+
+  // RoPE table: angle p * theta^(-2j/hd), computed in double on the host.
+  {
+    std::vector<float> t((size_t)cfg->max_seq * (hd / 2) * 2);
+    for (int p = 0; p < cfg->max_seq; ++p)
+      for (int j = 0; j < hd / 2; ++j) {
+        double a = (double)p * std::pow(cfg->rope_theta, -2.0 * j / hd);
+        t[((size_t)p * (hd / 2) + j) * 2] = (float)std::cos(a);
+        t[((size_t)p * (hd / 2) + j) * 2 + 1] = (float)std::sin(a);
+      }
+    if (hipMemcpy(h->rope, t.data(), t.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+      hipFree(h->ws);
+      delete h;
+      return MK_ERR_HIP;
+    }
+  }
+  // per-layer weight pointers
+  {
+    std::vector<LayerW> lw(L);
+    for (int l = 0; l < L; ++l) {
+      lw[l].attn_norm = (const uint16_t*)w->attn_norm[l];
+      lw[l].q = (const uint16_t*)w->q_proj[l];
+      lw[l].k = (const uint16_t*)w->k_proj[l];
+      lw[l].v = (const uint16_t*)w->v_proj[l];
+      lw[l].o = (const uint16_t*)w->o_proj[l];
+      lw[l].q_norm = cfg->qk_norm ? (const uint16_t*)w->q_norm[l] : nullptr;
+      lw[l].k_norm = cfg->qk_norm ? (const uint16_t*)w->k_norm[l] : nullptr;
+      lw[l].mlp_norm = (const uint16_t*)w->mlp_norm[l];
+      lw[l].gate = (const uint16_t*)w->gate_proj[l];
+      lw[l].up = (const uint16_t*)w->up_proj[l];
+      lw[l].down = (const uint16_t*)w->down_proj[l];
+    }
+    if (hipMalloc(&h->d_layers, sizeof(LayerW) * L) != hipSuccess) {
+      hipFree(h->ws);
+      delete h;
+      return MK_ERR_OOM;
+    }
+    if (hipMemcpy(h->d_layers, lw.data(), sizeof(LayerW) * L, hipMemcpyHostToDevice) != hipSuccess) {
+      hipFree(h->d_layers);
+      hipFree(h->ws);
+      delete h;
+      return MK_ERR_HIP;
+    }
+  }
+  h->embed = (const uint16_t*)w->embed;
+  h->lm_head = cfg->tied_embeddings ? (const uint16_t*)w->embed : (const uint16_t*)w->lm_head;
+  h->final_norm = (const uint16_t*)w->final_norm;
+  *out = h;
+  return MK_OK;
+}
+
+static void free_graph(GraphDev& g) {
+  hipFree(g.d_tasks);
+  hipFree(g.d_off);
+  hipFree(g.d_expect);
+  hipFree(g.d_part);
+  hipFree(g.d_grp);
+  free_plan(&g.plan);
+}
+
+static int get_graph(mk_handle* h, int b, GraphDev** out) {
+  auto it = h->graphs.find(b);
+  if (it != h->graphs.end()) {
+    *out = &it->second;
+    return MK_OK;
+  }
+  GraphDev g;
+  PlanCfg pc = plan_cfg(&h->cfg, h->ncu, h->xb, h->mfma_min_batch);
+  int rc = build_plan(pc, b, &g.plan);
+  if (rc) return rc;
+  const Plan& P = g.plan;
+  bool ok = hipMalloc(&g.d_tasks, sizeof(Task) * (size_t)std::max(1, P.n_tasks)) == hipSuccess &&
+            hipMalloc(&g.d_off, sizeof(int) * (h->ncu + 1)) == hipSuccess &&
+            hipMalloc(&g.d_expect, sizeof(int) * (size_t)P.n_counters * kShards) == hipSuccess &&
+            hipMalloc(&g.d_part, sizeof(float) * 1024 * (size_t)std::max(1, P.part_blocks)) == hipSuccess &&
+            hipMalloc(&g.d_grp, sizeof(uint32_t) * (size_t)std::max(1, P.grp_counters)) == hipSuccess;
+  if (!ok) {
+    free_graph(g);
+    return MK_ERR_OOM;
+  }
+  ok = hipMemcpy(g.d_tasks, P.tasks, sizeof(Task) * P.n_tasks, hipMemcpyHostToDevice) == hipSuccess &&
+       hipMemcpy(g.d_off, P.task_off, sizeof(int) * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
+       hipMemcpy(g.d_expect, P.expect, sizeof(int) * (size_t)P.n_counters * kShards, hipMemcpyHostToDevice) == hipSuccess &&
+       hipMemset(g.d_grp, 0, sizeof(uint32_t) * (size_t)std::max(1, P.grp_counters)) == hipSuccess;
+  if (!ok) {
+    free_graph(g);
+    return MK_ERR_HIP;
+  }
+  auto res = h->graphs.emplace(b, g);
+  *out = &res.first->second;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                   const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out, int32_t* next_tokens_out,
+                   void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (batch < 0 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+  if (batch == 0) return MK_OK;
+  if (!tokens || !positions || !seq_lens || !kv || !kv->k || !kv->v || !logits_out) return MK_ERR_INVALID_ARG;
+  if (kv->batch_cap < batch || kv->seq_cap < 1) return MK_ERR_INVALID_ARG;
+  GraphDev* g = nullptr;
+  int rc = get_graph(h, batch, &g);
+  if (rc) return rc;
+  const mk_model_cfg& c = h->cfg;
+  DevArgs A;
+  memset(&A, 0, sizeof(A));
+  A.L = c.n_layers;
+  A.d = c.hidden;
+  A.nq = c.n_q_heads;
+  A.nkv = c.n_kv_heads;
+  A.hd = c.head_dim;
+  A.G = c.n_q_heads / c.n_kv_heads;
+  A.I = c.intermediate;
+  A.V = c.vocab;
+  A.qdim = c.n_q_heads * c.head_dim;
+  A.kvdim = c.n_kv_heads * c.head_dim;
+  A.nqkv = A.qdim + 2 * A.kvdim;
+  A.qk_norm = c.qk_norm;
+  A.max_seq = c.max_seq;
+  A.eps = c.rms_eps;
+  A.layers = h->d_layers;
+  A.embed = h->embed;
+  A.lm_head = h->lm_head;
+  A.final_norm = h->final_norm;
+  A.kc = (uint16_t*)kv->k;
+  A.vc = (uint16_t*)kv->v;
+  A.kv_bcap = kv->batch_cap;
+  A.kv_scap = kv->seq_cap;
+  A.tokens = tokens;
+  A.positions = positions;
+  A.seq_lens = seq_lens;
+  A.logits = logits_out;
+  A.next_tokens = next_tokens_out;
+  A.b = batch;
+  A.bank = (int)(h->step & 1);
+  A.bcap = c.max_batch;
+  A.hres = h->hres;
+  A.hmid = h->hmid;
+  A.xattn = h->xattn;
+  A.xmlp = h->xmlp;
+  A.ssattn = h->ssattn;
+  A.ssmlp = h->ssmlp;
+  A.qkv = h->qkv;
+  A.attn_out = h->attn_out;
+  A.act = h->act;
+  A.part = g->d_part;
+  A.apart = h->apart;
+  A.banks = h->banks;
+  A.grp_ctr = g->d_grp;
+  A.seg_ctr = h->seg_ctr;
+  A.status = h->status;
+  A.rope = h->rope;
+  A.tasks = g->d_tasks;
+  A.task_off = g->d_off;
+  A.expect = g->d_expect;
+  A.ctr_stride = h->ctr_stride;
+  A.bank_words = h->bank_words;
+  for (int i = 0; i < 6; ++i) A.grp_off[i] = g->plan.grp_off[i];
+  A.ncu = h->ncu;
+  A.nslot = h->nslot;
+  A.xb_bytes = h->xb;
+  A.mfma = g->plan.mfma;
+  A.timeout_ticks = h->timeout_ticks;
+  if (launch_step(A, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  h->step += 1;
+  return MK_OK;
+}
+
+int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream) {
+  if (!h || !dst || batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+  const size_t row = (size_t)batch * h->cfg.hidden * 4;
+  const size_t spitch = (size_t)h->cfg.max_batch * h->cfg.hidden * 4;
+  if (hipMemcpy2DAsync(dst, row, h->hres, spitch, row, h->cfg.n_layers + 1, hipMemcpyDeviceToDevice,
+                       (hipStream_t)stream) != hipSuccess)
+    return MK_ERR_HIP;
+  return MK_OK;
+}
+
+int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* stream) {
+  if (!h || !dst || batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+  const mk_model_cfg& c = h->cfg;
+  const int qdim = c.n_q_heads * c.head_dim, nqkv = qdim + 2 * c.n_kv_heads * c.head_dim;
+  const void* src = nullptr;
+  size_t width = 0, esize = 4, layers = c.n_layers;
+  switch (which) {
+    case MK_STATE_HIDDEN: src = h->hres; width = c.hidden; layers = c.n_layers + 1; break;
+    case MK_STATE_HMID: src = h->hmid; width = c.hidden; break;
+    case MK_STATE_QKV: src = h->qkv; width = nqkv; break;
+    case MK_STATE_ATTN: src = h->attn_out; width = qdim; esize = 2; break;
+    case MK_STATE_ACT: src = h->act; width = c.intermediate; esize = 2; break;
+    default: return MK_ERR_INVALID_ARG;
+  }
+  const size_t row = (size_t)batch * width * esize, spitch = (size_t)c.max_batch * width * esize;
+  if (hipMemcpy2DAsync(dst, row, src, spitch, row, layers, hipMemcpyDeviceToDevice, (hipStream_t)stream) !=
+      hipSuccess)
+    return MK_ERR_HIP;
+  return MK_OK;
+}
+
+int mk_get_status(mk_handle* h, void* stream, uint32_t* status) {
+  if (!h || !status) return MK_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  uint32_t s[2];
+  if (hipMemcpy(s, h->status, 8, hipMemcpyDeviceToHost) != hipSuccess) return MK_ERR_HIP;
+  *status = s[0];
+  if (s[0] && hipMemset(h->status, 0, 4) != hipSuccess) return MK_ERR_HIP;
+  return MK_OK;
+}
+
+int mk_reset(mk_handle* h, void* stream) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  bool ok = hipMemset(h->banks, 0, (size_t)2 * h->bank_words * 4) == hipSuccess &&
+            hipMemset(h->seg_ctr, 0, (size_t)h->cfg.max_batch * h->cfg.n_kv_heads * 4) == hipSuccess &&
+            hipMemset(h->status, 0, 8) == hipSuccess;
+  for (auto& kv : h->graphs)
+    ok = ok && hipMemset(kv.second.d_grp, 0, sizeof(uint32_t) * (size_t)std::max(1, kv.second.plan.grp_counters)) == hipSuccess;
+  ok = ok && hipDeviceSynchronize() == hipSuccess;
+  return ok ? MK_OK : MK_ERR_HIP;
+}
+
+int mk_destroy(mk_handle* h) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  for (auto& kv : h->graphs) free_graph(kv.second);
+  hipFree(h->d_layers);
+  hipFree(h->ws);
+  delete h;
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Internal definitions shared by the host planner/runtime and the device kernel.
+#pragma once
+#include <stdint.h>
+
+// Helpers used by both the host planner and the device kernel.
+#if defined(__HIP__)
+#define MK_HD __host__ __device__
+#else
+#define MK_HD
+#endif
+
+namespace mk {
+
+// Work-group shape: compute waves wait on dependencies and do the math;
+// loader waves stream weights and cached K/V rows into an LDS ring and never
+// wait on a dependency counter.
+constexpr int kComputeWaves = 4;
+constexpr int kLoaderWaves = 4;
+constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
+constexpr int kComputeThreads = 64 * kComputeWaves;
+constexpr int kChunkBytes = 16384;          // one LDS ring slot
+constexpr int kWaveLoads = kChunkBytes / 1024;  // 16 B per lane x 64 lanes per wave-load
+constexpr int kMaxSlots = 8;
+constexpr int kShards = 64;                  // dependency counters are sharded 64 ways
+constexpr int kMaxBatch = 16;
+constexpr int kMaxGroup = 8;                 // n_q / n_kv
+constexpr int kValuBlock = 512;              // K elements per VALU k-block (64 lanes x 8)
+// LDS for cross-wave reductions: GEMV partial tiles (4 waves x 4 KB) or two
+// piece-parity buffers of attention states (4 waves x group x (head_dim + 4)
+// floats), whichever is larger for group <= 4 at head_dim 128 and group <= 8
+// at head_dim 64.
+constexpr int kRedBytes = 2 * 4 * 8 * (64 + 4) * 4;
+constexpr int kApartGroup = 8;               // group slots per attention partial
+
+enum Stage : int32_t { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_LM = 5, ST_EMBED = 6 };
+enum TaskType : int32_t { TT_EMBED = 1, TT_GEMV = 2, TT_ATTN = 3 };
+
+// One instruction of a CU's stream (64 bytes).
+struct Task {
+  int32_t type;
+  int32_t stage;
+  int32_t layer;
+  int32_t row0;        // GEMV: first logical output row; EMBED: first column
+  int32_t nsub;        // GEMV: 16-row sub-tiles; EMBED: number of columns
+  int32_t k0, k1;      // GEMV: K range
+  int32_t ks, nks;     // GEMV: K-split index and count
+  int32_t group;       // GEMV split-K group (counter index within the stage), -1 if nks == 1
+  int32_t part_slot;   // GEMV split-K: index of this group's partial block
+  int32_t wait_ctr;    // dependency counter to wait on, -1 = none
+  int32_t signal_ctr;  // counter this task signals when its outputs are complete
+  int32_t nchunks;     // GEMV: LDS chunks streamed by the loader
+  int32_t pad[2];
+};
+static_assert(sizeof(Task) == 64, "Task must be 64 bytes");
+
+// Counter indices: EMBED, then 5 per layer, then LM.
+MK_HD inline int ctr_embed() { return 0; }
+MK_HD inline int ctr_stage(int layer, int stage) { return 1 + 5 * layer + stage; }  // stage in QKV..DOWN
+MK_HD inline int ctr_lm(int n_layers) { return 1 + 5 * n_layers; }
+MK_HD inline int n_counters(int n_layers) { return 2 + 5 * n_layers; }
+// shard k of counter c lives at word k * stride + c; stride >= 32 words keeps
+// shards of one counter on different 128-byte lines.
+MK_HD inline int ctr_stride(int n_layers) {
+  int n = n_counters(n_layers);
+  return n < 32 ? 32 : n;
+}
+
+struct LayerW {
+  const uint16_t* attn_norm;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* q_norm;
+  const uint16_t* k_norm;
+  const uint16_t* mlp_norm;
+  const uint16_t* gate;
+  const uint16_t* up;
+  const uint16_t* down;
+};
+
+// Kernel argument block (passed by value).
+struct DevArgs {
+  // model shape
+  int32_t L, d, nq, nkv, hd, G, I, V, qdim, kvdim, nqkv;
+  int32_t qk_norm, max_seq;
+  float eps;
+  // weights
+  const LayerW* layers;
+  const uint16_t* embed;
+  const uint16_t* lm_head;
+  const uint16_t* final_norm;
+  // caller buffers
+  uint16_t* kc;
+  uint16_t* vc;
+  int32_t kv_bcap, kv_scap;
+  const int32_t* tokens;
+  const int32_t* positions;
+  const int32_t* seq_lens;
+  float* logits;
+  int32_t* next_tokens;
+  int32_t b;
+  int32_t bank;
+  // workspace (library-owned)
+  int32_t bcap;         // workspace batch capacity
+  float* hres;          // [L+1][bcap][d]
+  float* hmid;          // [L][bcap][d]
+  uint16_t* xattn;      // [L+1][bcap][d]  bf16(h * norm weight): GEMV input of QKV / LM head
+  uint16_t* xmlp;       // [L][bcap][d]    bf16(h_mid * norm weight): GEMV input of gate/up
+  float* ssattn;        // [L+1][d/16][bcap] partial sums of squares per 16-row tile
+  float* ssmlp;         // [L][d/16][bcap]
+  float* qkv;           // [L][bcap][nqkv]
+  uint16_t* attn_out;   // [L][bcap][qdim]
+  uint16_t* act;        // [L][bcap][I]
+  float* part;          // split-K partial blocks, 1024 floats each
+  float* apart;         // attention partials [ncu + bcap*nkv][group][hd + 4]
+  uint32_t* banks;      // 2 banks of kShards * ctr_stride words, then keys
+  uint32_t* grp_ctr;    // split-K group counters (self-resetting)
+  uint32_t* seg_ctr;    // attention segment counters [bcap*nkv] (self-resetting)
+  uint32_t* status;     // [0] status bits, [1] abort flag
+  const float* rope;    // [max_seq][hd/2][2] (cos, sin)
+  // schedule
+  const Task* tasks;
+  const int32_t* task_off;  // [ncu + 1]
+  const int32_t* expect;    // [n_counters][kShards]
+  int32_t ctr_stride;
+  int32_t bank_words;       // words per bank (counters + keys)
+  int32_t grp_off[6];       // per-stage base into grp_ctr
+  int32_t ncu;
+  int32_t nslot;
+  int32_t xb_bytes;
+  int32_t mfma;
+  uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
+};
+
+// Host planner --------------------------------------------------------------
+struct PlanCfg {
+  int L, d, nq, nkv, hd, I, V;
+  int ncu;
+  int xb_bytes;         // LDS bytes available to stage a GEMV input slice
+  int mfma_min_batch;   // batch at or above which projections use MFMA tiles
+};
+
+struct Plan {
+  int batch = 0;
+  int mfma = 0;
+  int n_tasks = 0;
+  int max_tasks_per_cu = 0;
+  int n_counters = 0;
+  int part_blocks = 0;                 // split-K partial blocks needed
+  int grp_counters = 0;
+  int grp_off[6] = {0, 0, 0, 0, 0, 0};
+  int stage_tasks[6] = {0, 0, 0, 0, 0, 0};
+  int stage_ksplit[6] = {0, 0, 0, 0, 0, 0};
+  int stage_rows[6] = {0, 0, 0, 0, 0, 0};
+  long long weight_bytes = 0;
+  long long max_cu_weight_bytes = 0;
+  double balance_min = 1.0;
+  // flattened streams
+  Task* tasks = nullptr;     // host copy, n_tasks
+  int* task_off = nullptr;   // ncu + 1
+  int* expect = nullptr;     // n_counters * kShards
+};
+
+// Builds and validates the per-CU streams; returns 0 or an MK_ERR_* code.
+int build_plan(const PlanCfg& pc, int batch, Plan* out);
+void free_plan(Plan* p);
+
+}  // namespace mk

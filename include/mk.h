@@ -1,0 +1,173 @@
+/* mk.h -- C ABI of an MI355X (gfx950) decode-step megakernel.
+ *
+ * One call of mk_decode_step runs one auto-regressive decode step of a
+ * Llama/Qwen3-style decoder for a ragged batch as ONE persistent HIP launch:
+ * embedding gather, per-layer RMSNorm, QKV projection, optional per-head QK
+ * RMSNorm, rotate-half RoPE at each sequence's own position, KV-cache store,
+ * attention over the cached positions, O projection, SwiGLU MLP, final
+ * RMSNorm, LM head and greedy argmax.  This is the decode step of the
+ * ForgeMegakernel paper summary ("2.1 The decode step"), kept inside one host
+ * launch as its "2.3 Megakernels" section describes, with per-CU instruction
+ * streams and dependency counters in place of grid-wide barriers ("4.1 The
+ * universal knowledge base and the milestones"; Cohere engine digest:
+ * persistent kernel with one block per SM, task descriptors, counter-based
+ * barriers in global memory, weights streamed before their activation
+ * dependencies are met).
+ *
+ * Conventions for every entry point:
+ *   - returns MK_OK (0) or a negative MK_ERR_* code; nothing aborts and no
+ *     exception crosses the ABI;  mk_error_string() names a code;
+ *   - "device pointer" means memory of the GPU the handle was created on;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *   - a handle may be used by one host thread / one stream at a time.
+ */
+#ifndef MK_H_
+#define MK_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_OK 0
+#define MK_ERR_INVALID_ARG (-1)   /* a NULL pointer, a size out of range, batch > max_batch ... */
+#define MK_ERR_UNSUPPORTED (-2)   /* a shape this build does not handle (head_dim not 64/128 ...) */
+#define MK_ERR_OOM (-3)           /* device allocation failed */
+#define MK_ERR_HIP (-4)           /* a HIP runtime call failed */
+#define MK_ERR_PLAN (-5)          /* the schedule failed validation (never expected) */
+
+/* Device status bits (mk_get_status).  Each bad value is clamped on the
+ * device so nothing is read or written out of bounds. */
+#define MK_STATUS_BAD_TOKEN 1u     /* tokens[i] outside [0, vocab)                  */
+#define MK_STATUS_BAD_POSITION 2u  /* positions[i] outside [0, min(max_seq, seq_cap)) */
+#define MK_STATUS_BAD_SEQLEN 4u    /* seq_lens[i] != positions[i] + 1               */
+#define MK_STATUS_TIMEOUT 8u       /* a dependency wait exceeded the spin limit; the
+                                      step was abandoned and the handle needs mk_reset */
+
+typedef struct mk_handle mk_handle;   /* opaque, owned by the library */
+
+/* Model shape.  Runtime values, not compile-time constants. */
+typedef struct {
+  int32_t n_layers;        /* >= 1 */
+  int32_t hidden;          /* d, multiple of 64 */
+  int32_t n_q_heads;       /* multiple of n_kv_heads, n_q_heads / n_kv_heads <= 8 */
+  int32_t n_kv_heads;
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t intermediate;    /* SwiGLU width, multiple of 64 */
+  int32_t vocab;
+  int32_t tied_embeddings; /* 1: the LM head is the embedding table */
+  int32_t qk_norm;         /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
+  double rope_theta;       /* RoPE base; frequency j = theta^(-2j/head_dim), rotate-half pairs */
+  float rms_eps;           /* RMSNorm epsilon (all norms) */
+  int32_t max_batch;       /* 1..16: largest batch any step will use */
+  int32_t max_seq;         /* positions must be < max_seq (sizes the RoPE table) */
+} mk_model_cfg;
+
+/* Weight pointers: DEVICE pointers to bf16 tensors in Hugging Face layout
+ * (linear weights [out, in] row-major; norm weights [n]).  The per-layer
+ * fields are HOST arrays of n_layers device pointers.  The caller owns all
+ * weights; they are never copied and must outlive the handle. */
+typedef struct {
+  const void* embed;       /* [vocab, hidden] */
+  const void* lm_head;     /* [vocab, hidden]; NULL iff tied_embeddings */
+  const void* final_norm;  /* [hidden] */
+  const void* const* attn_norm;  /* [hidden] */
+  const void* const* q_proj;     /* [n_q_heads*head_dim, hidden] */
+  const void* const* k_proj;     /* [n_kv_heads*head_dim, hidden] */
+  const void* const* v_proj;     /* [n_kv_heads*head_dim, hidden] */
+  const void* const* o_proj;     /* [hidden, n_q_heads*head_dim] */
+  const void* const* q_norm;     /* [head_dim]; NULL array unless qk_norm */
+  const void* const* k_norm;     /* [head_dim]; NULL array unless qk_norm */
+  const void* const* mlp_norm;   /* [hidden] */
+  const void* const* gate_proj;  /* [intermediate, hidden] */
+  const void* const* up_proj;    /* [intermediate, hidden] */
+  const void* const* down_proj;  /* [hidden, intermediate] */
+} mk_weight_ptrs;
+
+/* Caller-owned bf16 KV cache, DEVICE memory, layout
+ * [n_layers][batch_cap][n_kv_heads][seq_cap][head_dim]; row i holds sequence
+ * i.  K rows are stored after QK-norm and RoPE, V rows as projected. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t batch_cap;
+  int32_t seq_cap;
+} mk_kv_cache;
+
+/* Create a handle: validates the shape, allocates the library-owned
+ * workspace (per-layer activations, partial sums, counters, RoPE table) on
+ * the current HIP device.  *out is set only on success. */
+int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out);
+
+/* One greedy decode step for sequences 0..batch-1 (cache rows 0..batch-1),
+ * enqueued on `stream` as one kernel launch; returns without synchronising.
+ *   tokens[batch]     device int32: the token each sequence feeds now;
+ *   positions[batch]  device int32: its decode position p_i; the new K/V row
+ *                     is written to cache slot p_i and RoPE uses p_i;
+ *   seq_lens[batch]   device int32: rows attended after the write, must be
+ *                     p_i + 1 (checked on the device);
+ *   logits_out        device float [batch][vocab], written;
+ *   next_tokens_out   device int32 [batch] greedy argmax (lowest index wins a
+ *                     tie), written; may be NULL.
+ * batch == 0 is a no-op.  Errors detectable on the host return an error code
+ * before anything is enqueued; data errors are reported by mk_get_status. */
+int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                   const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
+                   int32_t* next_tokens_out, void* stream);
+
+/* Copy the residual stream of the last step, enqueued on `stream`:
+ * dst [n_layers+1][batch][hidden] float, entry l = input of layer l (entry 0
+ * is the gathered embedding, entry n_layers leaves the last layer). */
+int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream);
+
+/* Copy one per-layer mid-state buffer of the last step, enqueued on
+ * `stream`, for sequences 0..batch-1 of every layer, into dst (layout
+ * [layers][batch][width], dtype as listed):
+ *   MK_STATE_HIDDEN   float, L+1 layers, width hidden (same as mk_copy_hidden)
+ *   MK_STATE_HMID     float, L, hidden: residual after attention + O proj
+ *   MK_STATE_QKV      float, L, (n_q+2 n_kv) head_dim: raw q|k|v projections
+ *   MK_STATE_ATTN     bf16,  L, n_q head_dim: attention output per head
+ *   MK_STATE_ACT      bf16,  L, intermediate: silu(gate) * up
+ * Returns MK_ERR_INVALID_ARG for an unknown `which`. */
+#define MK_STATE_HIDDEN 0
+#define MK_STATE_HMID 1
+#define MK_STATE_QKV 2
+#define MK_STATE_ATTN 3
+#define MK_STATE_ACT 4
+int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* stream);
+
+/* Synchronise `stream`, return the device status bits accumulated since the
+ * last call in *status and clear them. */
+int mk_get_status(mk_handle* h, void* stream, uint32_t* status);
+
+/* Synchronise `stream` and clear all counters and status (needed after a
+ * MK_STATUS_TIMEOUT). */
+int mk_reset(mk_handle* h, void* stream);
+
+/* Free library-owned memory.  The caller's weights and caches are untouched. */
+int mk_destroy(mk_handle* h);
+
+const char* mk_error_string(int code);
+
+/* Schedule inspection, host only (no GPU needed): build and validate the
+ * per-CU instruction streams for `batch` on `n_cu` compute units. */
+typedef struct {
+  int32_t n_tasks;
+  int32_t max_tasks_per_cu;
+  int32_t n_counters;
+  int32_t mfma;                 /* 1 if the projection tiles use MFMA */
+  int64_t weight_bytes;         /* weight bytes covered by GEMV tasks (all layers + LM head) */
+  int64_t max_cu_weight_bytes;  /* largest per-CU share */
+  double stage_balance_min;     /* min over GEMV stages of mean/max bytes per CU */
+  int32_t stage_tasks[6];       /* tasks per layer-0 stage: QKV, ATTN, O, GU, DOWN, and LM */
+  int32_t stage_ksplit[6];      /* K-splits chosen per stage (ATTN entry 0) */
+  int32_t stage_rows_per_task[6];
+} mk_plan_stats;
+
+int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H_ */
