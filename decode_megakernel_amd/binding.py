@@ -57,8 +57,8 @@ class PlanStats(ctypes.Structure):
                 ("stage_rows_per_task", ctypes.c_int32 * 6)]
 
 
-EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_get_status", "mk_reset",
-           "mk_destroy", "mk_error_string", "mk_plan"]
+EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
+           "mk_reset", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
 
 _lib = None
@@ -76,6 +76,7 @@ def lib():
     L.mk_decode_step.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp]
     L.mk_copy_hidden.argtypes = [vp, i32, vp, vp]
     L.mk_copy_state.argtypes = [vp, i32, i32, vp, vp]
+    L.mk_copy_trace.argtypes = [vp, vp, ctypes.c_int64, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
     L.mk_get_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.mk_reset.argtypes = [vp, vp]
     L.mk_destroy.argtypes = [vp]
@@ -190,6 +191,22 @@ class DecodeEngine:
         out = torch.empty((nl, batch, width), dtype=dt, device="cuda")
         self.copy_state(which, batch, out)
         return out
+
+    def trace(self):
+        """(per-task records [n_cu, cap, 4] uint64, per-CU wait stats [n_cu, 32] uint64) of
+        the last step, or None when the handle was created without MK_TRACE."""
+        import torch
+        n_cu, cap = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().mk_copy_trace(self.handle, None, 0, ctypes.byref(n_cu), ctypes.byref(cap), None),
+               "mk_copy_trace")
+        if cap.value <= 0:
+            return None
+        n, c = n_cu.value, cap.value
+        buf = torch.empty(n * c * 4 + n * 32, dtype=torch.int64, device="cuda")
+        _check(lib().mk_copy_trace(self.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel() * 8,
+                                   ctypes.byref(n_cu), ctypes.byref(cap), _stream_handle(None)), "mk_copy_trace")
+        arr = buf.cpu().numpy().view("uint64")
+        return arr[: n * c * 4].reshape(n, c, 4), arr[n * c * 4:].reshape(n, 32)
 
     def status(self, stream=None) -> int:
         s = ctypes.c_uint32()

@@ -55,12 +55,14 @@ struct mk_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   // workspace views
-  float *hres, *hmid, *ssattn, *ssmlp, *qkv, *apart, *rope;
+  float *hres, *hmid, *ssattn, *ssmlp, *qkv, *apart, *rope, *zero;
   uint16_t *xattn, *xmlp, *attn_out, *act;
   uint32_t *banks, *seg_ctr, *status;
   int ctr_stride = 0, bank_words = 0;
   std::map<int, GraphDev> graphs;
   uint64_t step = 0;
+  uint64_t* trace = nullptr;   // MK_TRACE=<tasks per CU>: per-task timestamps + per-CU wait totals
+  int trace_cap = 0;
 };
 
 extern "C" {
@@ -117,7 +119,7 @@ int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats*
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!out || n_cu < 1 || batch < 1 || batch > cfg->max_batch) return MK_ERR_INVALID_ARG;
-  const int nslot = env_int("MK_NSLOT", 6);
+  const int nslot = env_int("MK_NSLOT", 7);
   PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot), env_int("MK_MFMA_MIN_BATCH", 8));
   Plan P;
   rc = build_plan(pc, batch, &P);
@@ -168,8 +170,10 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   }
   h->ncu = env_int("MK_NUM_CU", prop.multiProcessorCount);
   if (h->ncu < 1 || h->ncu > prop.multiProcessorCount) h->ncu = prop.multiProcessorCount;
-  h->nslot = env_int("MK_NSLOT", 6);
-  if (h->nslot < kComputeWaves) h->nslot = kComputeWaves;
+  h->nslot = env_int("MK_NSLOT", 7);
+  // a loader wave publishes a chunk only after issuing its next one, so the
+  // ring must hold more chunks than there are loader waves
+  if (h->nslot < kLoaderWaves + 1) h->nslot = kLoaderWaves + 1;
   if (h->nslot > kMaxSlots) h->nslot = kMaxSlots;
   h->xb = xb_for((int)prop.sharedMemPerBlock, h->nslot);
   if (h->xb < 4096) {
@@ -204,13 +208,14 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   size_t o_seg = take((size_t)bc * nkv * 4);
   size_t o_status = take(64);
   size_t o_rope = take((size_t)cfg->max_seq * (hd / 2) * 2 * 4);
+  size_t o_zero = take(1024);
   h->ws_bytes = off;
   if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
     delete h;
     return MK_ERR_OOM;
   }
   if (hipMemset(h->ws, 0, h->ws_bytes) != hipSuccess) {
-    hipFree(h->ws);
+    (void)hipFree(h->ws);
     delete h;
     return MK_ERR_HIP;
   }
@@ -228,6 +233,7 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   h->seg_ctr = (uint32_t*)(h->ws + o_seg);
   h->status = (uint32_t*)(h->ws + o_status);
   h->rope = (float*)(h->ws + o_rope);
+  h->zero = (float*)(h->ws + o_zero);
 
   // RoPE table: angle p * theta^(-2j/hd), computed in double on the host.
   {
@@ -239,7 +245,7 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
         t[((size_t)p * (hd / 2) + j) * 2 + 1] = (float)std::sin(a);
       }
     if (hipMemcpy(h->rope, t.data(), t.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
-      hipFree(h->ws);
+      (void)hipFree(h->ws);
       delete h;
       return MK_ERR_HIP;
     }
@@ -261,15 +267,25 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
       lw[l].down = (const uint16_t*)w->down_proj[l];
     }
     if (hipMalloc(&h->d_layers, sizeof(LayerW) * L) != hipSuccess) {
-      hipFree(h->ws);
+      (void)hipFree(h->ws);
       delete h;
       return MK_ERR_OOM;
     }
     if (hipMemcpy(h->d_layers, lw.data(), sizeof(LayerW) * L, hipMemcpyHostToDevice) != hipSuccess) {
-      hipFree(h->d_layers);
-      hipFree(h->ws);
+      (void)hipFree(h->d_layers);
+      (void)hipFree(h->ws);
       delete h;
       return MK_ERR_HIP;
+    }
+  }
+  h->trace_cap = env_int("MK_TRACE", 0);
+  if (h->trace_cap > 0) {
+    size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * 32) * 8;
+    if (hipMalloc(&h->trace, tb) != hipSuccess || hipMemset(h->trace, 0, tb) != hipSuccess) {
+      (void)hipFree(h->d_layers);
+      (void)hipFree(h->ws);
+      delete h;
+      return MK_ERR_OOM;
     }
   }
   h->embed = (const uint16_t*)w->embed;
@@ -280,11 +296,11 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
 }
 
 static void free_graph(GraphDev& g) {
-  hipFree(g.d_tasks);
-  hipFree(g.d_off);
-  hipFree(g.d_expect);
-  hipFree(g.d_part);
-  hipFree(g.d_grp);
+  (void)hipFree(g.d_tasks);
+  (void)hipFree(g.d_off);
+  (void)hipFree(g.d_expect);
+  (void)hipFree(g.d_part);
+  (void)hipFree(g.d_grp);
   free_plan(&g.plan);
 }
 
@@ -381,6 +397,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.seg_ctr = h->seg_ctr;
   A.status = h->status;
   A.rope = h->rope;
+  A.zero = (const uint16_t*)h->zero;
   A.tasks = g->d_tasks;
   A.task_off = g->d_off;
   A.expect = g->d_expect;
@@ -392,6 +409,8 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.xb_bytes = h->xb;
   A.mfma = g->plan.mfma;
   A.timeout_ticks = h->timeout_ticks;
+  A.trace = h->trace;
+  A.trace_cap = h->trace_cap;
   if (launch_step(A, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   h->step += 1;
   return MK_OK;
@@ -428,6 +447,17 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
   return MK_OK;
 }
 
+int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t* cap, void* stream) {
+  if (!h || !n_cu || !cap) return MK_ERR_INVALID_ARG;
+  *n_cu = h->ncu;
+  *cap = h->trace_cap;
+  if (!h->trace || !dst) return MK_OK;
+  const size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * 32) * 8;
+  if (bytes < (int64_t)tb) return MK_ERR_INVALID_ARG;
+  if (hipMemcpyAsync(dst, h->trace, tb, hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  return MK_OK;
+}
+
 int mk_get_status(mk_handle* h, void* stream, uint32_t* status) {
   if (!h || !status) return MK_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
@@ -453,8 +483,9 @@ int mk_reset(mk_handle* h, void* stream) {
 int mk_destroy(mk_handle* h) {
   if (!h) return MK_ERR_INVALID_ARG;
   for (auto& kv : h->graphs) free_graph(kv.second);
-  hipFree(h->d_layers);
-  hipFree(h->ws);
+  (void)hipFree(h->trace);
+  (void)hipFree(h->d_layers);
+  (void)hipFree(h->ws);
   delete h;
   return MK_OK;
 }

@@ -24,7 +24,8 @@ constexpr int kMaxSlots = 8;
 constexpr int kShards = 64;                  // dependency counters are sharded 64 ways
 constexpr int kMaxBatch = 16;
 constexpr int kMaxGroup = 8;                 // n_q / n_kv
-constexpr int kValuBlock = 512;              // K elements per VALU k-block (64 lanes x 8)
+constexpr int kKBlock = 512;                 // K elements per chunk (64 lanes x 8 for VALU, 16 MFMA k-steps)
+constexpr int kGroupSub = 4;                 // 16-row sub-tiles per row group (one per compute wave)
 // LDS for cross-wave reductions: GEMV partial tiles (4 waves x 4 KB) or two
 // piece-parity buffers of attention states (4 waves x group x (head_dim + 4)
 // floats), whichever is larger for group <= 4 at head_dim 128 and group <= 8
@@ -41,15 +42,16 @@ struct Task {
   int32_t stage;
   int32_t layer;
   int32_t row0;        // GEMV: first logical output row; EMBED: first column
-  int32_t nsub;        // GEMV: 16-row sub-tiles; EMBED: number of columns
-  int32_t k0, k1;      // GEMV: K range
-  int32_t ks, nks;     // GEMV: K-split index and count
-  int32_t group;       // GEMV split-K group (counter index within the stage), -1 if nks == 1
-  int32_t part_slot;   // GEMV split-K: index of this group's partial block
+  int32_t nsub;        // GEMV: 16-row sub-tiles of the group (1..4); EMBED: number of columns
+  int32_t k0, k1;      // GEMV: K range, k0 a multiple of 512
+  int32_t ks, nks;     // GEMV: this task's piece index among the nks pieces that split the group's K
+  int32_t group;       // GEMV: row group (counter index within the stage when nks > 1)
+  int32_t part_slot;   // GEMV nks > 1: partial block of piece 0 of the group (piece k at part_slot + k)
   int32_t wait_ctr;    // dependency counter to wait on, -1 = none
   int32_t signal_ctr;  // counter this task signals when its outputs are complete
-  int32_t nchunks;     // GEMV: LDS chunks streamed by the loader
-  int32_t pad[2];
+  int32_t nchunks;     // GEMV: LDS chunks streamed by the loader (nsub x k-blocks)
+  int32_t flags;       // bit 0: signal signal_ctr after this task (the CU's last task of the stage)
+  int32_t pad;
 };
 static_assert(sizeof(Task) == 64, "Task must be 64 bytes");
 
@@ -119,6 +121,7 @@ struct DevArgs {
   uint32_t* seg_ctr;    // attention segment counters [bcap*nkv] (self-resetting)
   uint32_t* status;     // [0] status bits, [1] abort flag
   const float* rope;    // [max_seq][hd/2][2] (cos, sin)
+  const uint16_t* zero; // >= 16 zero bytes: the source of masked direct-to-LDS lanes
   // schedule
   const Task* tasks;
   const int32_t* task_off;  // [ncu + 1]
@@ -131,6 +134,8 @@ struct DevArgs {
   int32_t xb_bytes;
   int32_t mfma;
   uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
+  uint64_t* trace;          // optional per-task timestamps [ncu][trace_cap][4], NULL = off
+  int32_t trace_cap;
 };
 
 // Host planner --------------------------------------------------------------
@@ -140,6 +145,7 @@ struct PlanCfg {
   int xb_bytes;         // LDS bytes available to stage a GEMV input slice
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
 };
+constexpr int kTaskSignal = 1;
 
 struct Plan {
   int batch = 0;

@@ -28,6 +28,37 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 constexpr unsigned kCpSc1 = 16;  // cache policy: device scope (coherent across XCDs)
+
+// Kernel arguments are read in place from the kernarg segment through a
+// constant-address-space pointer; `uni` re-establishes at a function's entry
+// that the pointer is wave-uniform, so every field read is a scalar load and
+// never waits behind (or drains) the vector memory queue.
+#define MK_AS4 __attribute__((address_space(4)))
+typedef const MK_AS4 DevArgs* DArgs;
+__device__ __forceinline__ DArgs uni(DArgs p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (DArgs)(((unsigned long long)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ const MK_AS4 T* as_const(const T* p) {
+  return (const MK_AS4 T*)p;
+}
+typedef const MK_AS4 Task* TaskP;
+// copy a 64-byte task descriptor out of constant memory (scalar loads)
+__device__ __forceinline__ Task load_task(TaskP p) {
+  Task t;
+  const MK_AS4 int32_t* src = (const MK_AS4 int32_t*)p;
+  int32_t* dst = (int32_t*)&t;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Task) / 4); ++i) dst[i] = src[i];
+  return t;
+}
+__device__ __forceinline__ TaskP uni(TaskP p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (TaskP)(((unsigned long long)hi << 32) | lo);
+}
 constexpr uint32_t kStatusTimeout = 8u;
 
 // ---------------------------------------------------------------- helpers
@@ -108,8 +139,8 @@ __device__ __forceinline__ int lds_ld_acq(int* p) { return __hip_atomic_load(p, 
 __device__ __forceinline__ void lds_st_rel(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
 __device__ __forceinline__ bool lds_aborted(Ctrl* c) { return __hip_atomic_load(&c->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0; }
 
-__device__ __forceinline__ bool global_aborted(const DevArgs& A) {
-  return __hip_atomic_load(A.status + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+__device__ __forceinline__ bool global_aborted(DArgs A) {
+  return __hip_atomic_load(A->status + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
 // Every spin loop is bounded: on abort or after the time limit the CU gives
@@ -120,22 +151,22 @@ struct Spin {
   int it;
 };
 __device__ __forceinline__ Spin spin_start() { return Spin{now_ticks(), 0}; }
-__device__ __noinline__ bool spin_fail(const DevArgs& A, Ctrl* c) {
+__device__ __noinline__ bool spin_fail(const uint32_t* status, Ctrl* c) {
   if (__hip_atomic_load(&c->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return true;
-  if (global_aborted(A)) {
+  if (__hip_atomic_load(status + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
     __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return true;
   }
   return false;
 }
 // returns false when the wait must be abandoned
-__device__ __forceinline__ bool spin_ok(const DevArgs& A, Ctrl* c, Spin& sp) {
+__device__ __forceinline__ bool spin_ok(DArgs A, Ctrl* c, Spin& sp) {
   if (lds_aborted(c)) return false;
   if ((++sp.it & 63) == 0) {
-    if (spin_fail(A, c)) return false;
-    if (now_ticks() - sp.t0 > A.timeout_ticks) {
-      atomicOr(A.status, kStatusTimeout);
-      __hip_atomic_store(A.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (spin_fail(A->status, c)) return false;
+    if (now_ticks() - sp.t0 > A->timeout_ticks) {
+      atomicOr(A->status, kStatusTimeout);
+      __hip_atomic_store(A->status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return false;
     }
@@ -145,28 +176,31 @@ __device__ __forceinline__ bool spin_ok(const DevArgs& A, Ctrl* c, Spin& sp) {
 }
 
 // Software barrier among the compute waves (the loader waves never join).
-__device__ __forceinline__ bool cbar(const DevArgs& A, Ctrl* c, int& gen, int lane) {
+__device__ __forceinline__ bool cbar(DArgs A, Ctrl* c, int& gen, int lane, uint64_t* wait_ticks = nullptr) {
   ++gen;
   if (lane == 0) __hip_atomic_fetch_add(&c->bar, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   const int target = gen * kComputeWaves;
+  if (lds_ld_acq(&c->bar) >= target) return true;
   Spin sp = spin_start();
   while (lds_ld_acq(&c->bar) < target)
     if (!spin_ok(A, c, sp)) return false;
+  if (A->trace && wait_ticks) *wait_ticks += now_ticks() - sp.t0;
   return true;
 }
 
-__device__ __forceinline__ uint32_t* bank_ptr(const DevArgs& A, int which) {
-  return A.banks + (size_t)which * A.bank_words;
+__device__ __forceinline__ uint32_t* bank_ptr(DArgs A, int which) {
+  return A->banks + (size_t)which * A->bank_words;
 }
-__device__ __forceinline__ unsigned long long* keys_ptr(const DevArgs& A) {
-  return (unsigned long long*)(bank_ptr(A, A.bank) + kShards * A.ctr_stride);
+__device__ __forceinline__ unsigned long long* keys_ptr(DArgs A) {
+  return (unsigned long long*)(bank_ptr(A, A->bank) + kShards * A->ctr_stride);
 }
 
 // Wait (one wave, all 64 lanes) until every shard of counter `ctr` reached
 // the count the schedule expects.
-__device__ bool wait_counter(const DevArgs& A, Ctrl* c, int ctr, int lane) {
-  const uint32_t* p = bank_ptr(A, A.bank) + lane * A.ctr_stride + ctr;
-  const int e = A.expect[ctr * kShards + lane];
+__device__ bool wait_counter(DArgs A, Ctrl* c, int ctr, int lane) {
+  A = uni(A);
+  const uint32_t* p = bank_ptr(A, A->bank) + lane * A->ctr_stride + ctr;
+  const int e = as_const(A->expect)[ctr * kShards + lane];
   const uint64_t t0 = now_ticks();
   for (int it = 0;; ++it) {
     int v = (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -176,10 +210,10 @@ __device__ bool wait_counter(const DevArgs& A, Ctrl* c, int ctr, int lane) {
         __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return false;
       }
-      if (now_ticks() - t0 > A.timeout_ticks) {
+      if (now_ticks() - t0 > A->timeout_ticks) {
         if (lane == 0) {
-          atomicOr(A.status, kStatusTimeout);
-          __hip_atomic_store(A.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          atomicOr(A->status, kStatusTimeout);
+          __hip_atomic_store(A->status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return false;
@@ -189,66 +223,72 @@ __device__ bool wait_counter(const DevArgs& A, Ctrl* c, int ctr, int lane) {
   }
 }
 
-__device__ __forceinline__ void signal_counter(const DevArgs& A, int ctr, int cu) {
-  uint32_t* p = bank_ptr(A, A.bank) + (cu % kShards) * A.ctr_stride + ctr;
+__device__ __forceinline__ void signal_counter(DArgs A, int ctr, int cu) {
+  uint32_t* p = bank_ptr(A, A->bank) + (cu % kShards) * A->ctr_stride + ctr;
   __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------- stage geometry
-__device__ __forceinline__ int stage_M(const DevArgs& A, int st) {
+__device__ __forceinline__ int stage_M(DArgs A, int st) {
   switch (st) {
-    case ST_QKV: return A.nqkv;
-    case ST_O: return A.d;
-    case ST_GU: return 2 * A.I;
-    case ST_DOWN: return A.d;
-    default: return A.V;
+    case ST_QKV: return A->nqkv;
+    case ST_O: return A->d;
+    case ST_GU: return 2 * A->I;
+    case ST_DOWN: return A->d;
+    default: return A->V;
   }
 }
-__device__ __forceinline__ int stage_K(const DevArgs& A, int st) {
+__device__ __forceinline__ int stage_K(DArgs A, int st) {
   switch (st) {
-    case ST_O: return A.qdim;
-    case ST_DOWN: return A.I;
-    default: return A.d;
+    case ST_O: return A->qdim;
+    case ST_DOWN: return A->I;
+    default: return A->d;
   }
 }
 // bf16 input activation [bcap][K] of a GEMV stage
-__device__ __forceinline__ const uint16_t* stage_x(const DevArgs& A, int st, int l) {
+__device__ __forceinline__ const uint16_t* stage_x(DArgs A, int st, int l) {
   switch (st) {
-    case ST_QKV: return A.xattn + (size_t)l * A.bcap * A.d;
-    case ST_O: return A.attn_out + (size_t)l * A.bcap * A.qdim;
-    case ST_GU: return A.xmlp + (size_t)l * A.bcap * A.d;
-    case ST_DOWN: return A.act + (size_t)l * A.bcap * A.I;
-    default: return A.xattn + (size_t)A.L * A.bcap * A.d;  // LM head reads the final-normed input
+    case ST_QKV: return A->xattn + (size_t)l * A->bcap * A->d;
+    case ST_O: return A->attn_out + (size_t)l * A->bcap * A->qdim;
+    case ST_GU: return A->xmlp + (size_t)l * A->bcap * A->d;
+    case ST_DOWN: return A->act + (size_t)l * A->bcap * A->I;
+    default: return A->xattn + (size_t)A->L * A->bcap * A->d;  // LM head reads the final-normed input
   }
 }
-__device__ __forceinline__ const float* stage_ss(const DevArgs& A, int st, int l) {
-  const int nt = A.d / 16;
+__device__ __forceinline__ const float* stage_ss(DArgs A, int st, int l) {
+  const int nt = A->d / 16;
   switch (st) {
-    case ST_QKV: return A.ssattn + (size_t)l * nt * A.bcap;
-    case ST_GU: return A.ssmlp + (size_t)l * nt * A.bcap;
-    case ST_LM: return A.ssattn + (size_t)A.L * nt * A.bcap;
+    case ST_QKV: return A->ssattn + (size_t)l * nt * A->bcap;
+    case ST_GU: return A->ssmlp + (size_t)l * nt * A->bcap;
+    case ST_LM: return A->ssattn + (size_t)A->L * nt * A->bcap;
     default: return nullptr;
   }
 }
-// weight row `lr` (logical row of the stage) of layer l
-__device__ __forceinline__ const uint16_t* row_ptr(const DevArgs& A, int st, int l, int lr) {
+// weight row `lr` (logical row of the stage) of layer l.  Every candidate
+// base pointer is read unconditionally (uniform scalar loads) and the row's
+// matrix is chosen with selects, so a per-lane row never turns the pointer
+// table read into a per-lane memory access.
+__device__ __forceinline__ const uint16_t* row_ptr(DArgs A, int st, int l, int lr) {
   switch (st) {
     case ST_QKV: {
-      const LayerW& w = A.layers[l];
-      if (lr < A.qdim) return w.q + (size_t)lr * A.d;
-      lr -= A.qdim;
-      if (lr < A.kvdim) return w.k + (size_t)lr * A.d;
-      return w.v + (size_t)(lr - A.kvdim) * A.d;
+      const MK_AS4 LayerW* w = as_const(A->layers) + l;
+      const uint16_t *q = w->q, *k = w->k, *v = w->v;
+      const int qd = A->qdim, kd = A->kvdim;
+      const bool in_q = lr < qd, in_k = !in_q && lr < qd + kd;
+      const uint16_t* base = in_q ? q : (in_k ? k : v);
+      const int r = in_q ? lr : (in_k ? lr - qd : lr - qd - kd);
+      return base + (size_t)r * A->d;
     }
-    case ST_O: return A.layers[l].o + (size_t)lr * A.qdim;
+    case ST_O: return as_const(A->layers)[l].o + (size_t)lr * A->qdim;
     case ST_GU: {
       // logical tile t = 8 gate rows (8t..8t+7) followed by the same 8 up rows
-      const LayerW& w = A.layers[l];
-      int t = lr >> 4, j = lr & 15;
-      return (j < 8 ? w.gate : w.up) + (size_t)(8 * t + (j & 7)) * A.d;
+      const MK_AS4 LayerW* w = as_const(A->layers) + l;
+      const uint16_t *g = w->gate, *u = w->up;
+      const int t = lr >> 4, j = lr & 15;
+      return (j < 8 ? g : u) + (size_t)(8 * t + (j & 7)) * A->d;
     }
-    case ST_DOWN: return A.layers[l].down + (size_t)lr * A.I;
-    default: return A.lm_head + (size_t)lr * A.d;
+    case ST_DOWN: return as_const(A->layers)[l].down + (size_t)lr * A->I;
+    default: return A->lm_head + (size_t)lr * A->d;
   }
 }
 
@@ -261,6 +301,55 @@ struct Piece {
   int i, g, j0, j1, sid, ncached, nch, has_new;
   long long seg_start;
 };
+
+// Register-resident copy of the per-sequence attended lengths (the loader
+// waves must not read LDS through the compiler: see loader_main).
+struct SeqLens {
+  int v[kMaxBatch];
+};
+__device__ __forceinline__ long long attn_total_r(const SeqLens& sl, int b, int nkv) {
+  long long W = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxBatch; ++i)
+    if (i < b) W += sl.v[i];
+  return W * nkv;
+}
+__device__ __forceinline__ bool next_piece_r(const SeqLens& sl, int b, int nkv, int rpc, long long& pos, long long hi,
+                                             Piece& P) {
+  if (pos >= hi) return false;
+  long long acc = 0;
+  int i = 0, s = sl.v[0];
+  bool found = false;
+#pragma unroll
+  for (int k = 0; k < kMaxBatch; ++k) {
+    if (!found && k < b) {
+      const long long seg = (long long)nkv * sl.v[k];
+      if (pos < acc + seg || k == b - 1) {
+        i = k;
+        s = sl.v[k];
+        found = true;
+      } else {
+        acc += seg;
+      }
+    }
+  }
+  long long off = pos - acc;
+  P.i = i;
+  P.g = (int)(off / s);
+  P.j0 = (int)(off % s);
+  long long take = s - P.j0;
+  if (hi - pos < take) take = hi - pos;
+  P.j1 = P.j0 + (int)take;
+  P.sid = i * nkv + P.g;
+  P.seg_start = acc + (long long)P.g * s;
+  const int p = s - 1;
+  int nc = (P.j1 < p ? P.j1 : p) - P.j0;
+  P.ncached = nc > 0 ? nc : 0;
+  P.has_new = P.j1 == s;
+  P.nch = (P.ncached + rpc - 1) / rpc;
+  pos += take;
+  return true;
+}
 
 __device__ __forceinline__ long long attn_total(const Ctrl* c, int b, int nkv) {
   long long W = 0;
@@ -301,150 +390,280 @@ __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rp
 }
 
 // ================================================================ loader
-struct LDesc {
-  int task;     // index into this CU's stream
-  int local;    // chunk index within the task
-  int q;        // CU-global chunk sequence number
-};
+// The loader waves move weight tiles and cached K/V rows into the LDS ring
+// with direct-to-LDS loads (global_load_lds_dwordx4): no data registers, up
+// to two 16 KB chunks in flight per loader wave.  Their flag reads and
+// writes go through inline LDS instructions with explicit waits: the
+// compiler cannot tell a flag from the ring that the DMA writes, and would
+// otherwise drain every outstanding load before each flag access.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ int lds_flag_read(const int* p) {
+  int v;
+  __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_flag_write(int* p, int v) {
+  __asm__ volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+// vmcnt <= 16 (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+__device__ __forceinline__ void wait_vmcnt16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-struct LoaderIter {
-  int ti, nt, qbase, nchunks, entered, q;
-};
-
-__device__ int attn_task_chunks(const DevArgs& A, const Ctrl* c, int cu, int rpc) {
-  long long W = attn_total(c, A.b, A.nkv);
-  long long pos = cu_lo(cu, W, A.ncu), hi = cu_lo(cu + 1, W, A.ncu);
-  Piece P;
-  int n = 0;
-  while (next_piece(c, A.b, A.nkv, rpc, pos, hi, P)) n += P.nch;
-  return n;
+__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 2 /* nt */);
 }
 
-__device__ bool loader_next(const DevArgs& A, const Task* T, const Ctrl* c, int cu, int rpc, LoaderIter& it, LDesc& d) {
-  while (it.ti < it.nt) {
-    if (!it.entered) {
-      const Task& t = T[it.ti];
-      if (t.type == TT_GEMV) it.nchunks = t.nchunks;
-      else if (t.type == TT_ATTN) it.nchunks = attn_task_chunks(A, c, cu, rpc);
-      else it.nchunks = 0;
-      it.entered = 1;
+// Weight rows of one 16-row sub-tile: row j lives at (j < 8 ? b0 : b1) +
+// (j & 7) * stride; rows >= nrows are past the matrix and read zeros.
+struct RowBase {
+  const uint16_t* b0;
+  const uint16_t* b1;
+  long long stride;
+  int nrows;
+};
+
+__device__ __forceinline__ RowBase sub_rows(DArgs A, const Task& t, int sub) {
+  const int r = t.row0 + 16 * sub;
+  RowBase rb;
+  rb.nrows = min(16, stage_M(A, t.stage) - r);
+  const MK_AS4 LayerW* w = as_const(A->layers) + (t.stage == ST_LM ? 0 : t.layer);
+  switch (t.stage) {
+    case ST_QKV: {
+      const uint16_t *q = w->q, *k = w->k, *v = w->v;
+      const int qd = A->qdim, kd = A->kvdim;
+      const bool in_q = r < qd, in_k = !in_q && r < qd + kd;
+      const uint16_t* base = in_q ? q : (in_k ? k : v);
+      const int rr = in_q ? r : (in_k ? r - qd : r - qd - kd);
+      rb.stride = A->d;
+      rb.b0 = base + (size_t)rr * A->d;
+      rb.b1 = rb.b0 + (size_t)8 * A->d;
+      break;
     }
-    if (it.q < it.qbase + it.nchunks) {
-      d.task = it.ti;
-      d.local = it.q - it.qbase;
-      d.q = it.q;
-      it.q += kLoaderWaves;
-      return true;
+    case ST_O:
+      rb.stride = A->qdim;
+      rb.b0 = w->o + (size_t)r * A->qdim;
+      rb.b1 = rb.b0 + (size_t)8 * A->qdim;
+      break;
+    case ST_GU: {
+      // logical tile = 8 gate rows then the same 8 up rows
+      const int t16 = r >> 4;
+      rb.stride = A->d;
+      rb.b0 = w->gate + (size_t)(8 * t16) * A->d;
+      rb.b1 = w->up + (size_t)(8 * t16) * A->d;
+      break;
     }
-    it.qbase += it.nchunks;
-    it.ti += 1;
-    it.entered = 0;
+    case ST_DOWN:
+      rb.stride = A->I;
+      rb.b0 = w->down + (size_t)r * A->I;
+      rb.b1 = rb.b0 + (size_t)8 * A->I;
+      break;
+    default:
+      rb.stride = A->d;
+      rb.b0 = A->lm_head + (size_t)r * A->d;
+      rb.b1 = rb.b0 + (size_t)8 * A->d;
+      break;
   }
-  return false;
+  return rb;
 }
 
+// One GEMV chunk: 16 rows x 512 K (VALU: wave-load j = row j) or 16 MFMA
+// k-steps of 16 rows x 32 K in the A-operand lane layout.
+__device__ __forceinline__ void dma_gemv_chunk(DArgs A, const RowBase& rb, int kb, int k1, int lane, char* dst) {
+  if (!A->mfma) {
+    const int kk = kb * kKBlock + 8 * lane;
+    const bool kok = kk < k1;
+#pragma unroll
+    for (int j = 0; j < kWaveLoads; ++j) {
+      const uint16_t* src = (j < 8 ? rb.b0 : rb.b1) + (size_t)(j & 7) * rb.stride + kk;
+      dma16((kok && j < rb.nrows) ? (const void*)src : (const void*)A->zero, dst + j * 1024);
+    }
+  } else {
+    const int row = lane & 15;
+    const uint16_t* rp = (row < 8 ? rb.b0 : rb.b1) + (size_t)(row & 7) * rb.stride;
+    const bool rok = row < rb.nrows;
+    const int kk0 = kb * kKBlock + 8 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < kWaveLoads; ++j) {
+      const int kk = kk0 + 32 * j;
+      dma16((rok && kk < k1) ? (const void*)(rp + kk) : (const void*)A->zero, dst + j * 1024);
+    }
+  }
+}
+
+// One attention chunk: RPC cached K rows, then the same V rows.
 template <int HD>
-__device__ __forceinline__ void issue_attn_loads(const DevArgs& A, const Ctrl* c, const Task& t, int cu, int local, int lane, u32x4* r) {
-  constexpr int LPR = HD / 8, RP = 64 / LPR, RPC = 4096 / HD;
-  long long W = attn_total(c, A.b, A.nkv);
-  long long pos = cu_lo(cu, W, A.ncu), hi = cu_lo(cu + 1, W, A.ncu);
-  Piece P;
-  int base = 0;
-  while (next_piece(c, A.b, A.nkv, RPC, pos, hi, P)) {
-    if (local < base + P.nch) break;
-    base += P.nch;
-  }
-  const int ch = local - base;
-  const int rows = min(RPC, P.ncached - ch * RPC);
-  const size_t head = (((size_t)t.layer * A.kv_bcap + P.i) * A.nkv + P.g) * A.kv_scap;
+__device__ __forceinline__ void dma_attn_chunk(DArgs A, const uint16_t* kbase, const uint16_t* vbase, int rows, int lane,
+                                               char* dst) {
+  constexpr int LPR = HD / 8, RP = 64 / LPR;
   const int e = (lane % LPR) * 8;
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
     const int rl = (j & 7) * RP + lane / LPR;
-    const uint16_t* src = (j < 8 ? A.kc : A.vc) + (head + P.j0 + ch * RPC + rl) * HD + e;
-    r[j] = rl < rows ? nt_load16(src) : u32x4{0, 0, 0, 0};
+    const uint16_t* src = (j < 8 ? kbase : vbase) + (size_t)rl * HD + e;
+    dma16(rl < rows ? (const void*)src : (const void*)A->zero, dst + j * 1024);
   }
 }
 
-__device__ __forceinline__ void issue_gemv_loads(const DevArgs& A, const Task& t, int local, int lane, u32x4* r) {
-  const int M = stage_M(A, t.stage);
-  if (!A.mfma) {
-    const int kk = t.k0 + kValuBlock * local + 8 * lane;
-#pragma unroll
-    for (int j = 0; j < kWaveLoads; ++j) {
-      const int lr = t.row0 + j;
-      const bool ok = lr < M && kk < t.k1;
-      r[j] = ok ? nt_load16(row_ptr(A, t.stage, t.layer, lr) + kk) : u32x4{0, 0, 0, 0};
-    }
-  } else {
-    const int R = t.nsub, spc = kWaveLoads / R;
-#pragma unroll
-    for (int j = 0; j < kWaveLoads; ++j) {
-      const int s = j / R, rr = j % R;
-      const int kk = t.k0 + 32 * (local * spc + s) + 8 * (lane >> 4);
-      const int lr = t.row0 + 16 * rr + (lane & 15);
-      const bool ok = lr < M && kk < t.k1;
-      r[j] = ok ? nt_load16(row_ptr(A, t.stage, t.layer, lr) + kk) : u32x4{0, 0, 0, 0};
+// Wait until ring slot `slot` no longer holds an unconsumed chunk.
+__device__ __forceinline__ bool loader_wait_free(DArgs A, Ctrl* c, int slot, int need, uint64_t& wait_ticks) {
+  if (lds_flag_read(&c->freed[slot]) >= need) return true;
+  const uint64_t t0 = now_ticks();
+  for (int it = 0;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    if (lds_flag_read(&c->freed[slot]) >= need) break;
+    if (lds_flag_read(&c->abort)) return false;
+    if ((it & 255) == 255 && now_ticks() - t0 > A->timeout_ticks) {
+      atomicOr(A->status, kStatusTimeout);
+      __hip_atomic_store(A->status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_flag_write(&c->abort, 1);
+      return false;
     }
   }
-}
-
-__device__ __forceinline__ void issue_loads(const DevArgs& A, const Task* T, const Ctrl* c, int cu, const LDesc& d, int lane, u32x4* r) {
-  const Task& t = T[d.task];
-  if (t.type == TT_GEMV) issue_gemv_loads(A, t, d.local, lane, r);
-  else if (A.hd == 128) issue_attn_loads<128>(A, c, t, cu, d.local, lane, r);
-  else issue_attn_loads<64>(A, c, t, cu, d.local, lane, r);
-}
-
-__device__ __forceinline__ bool store_chunk(const DevArgs& A, char* ring, Ctrl* c, const LDesc& d, int lane, const u32x4* r) {
-  const int slot = d.q % A.nslot;
-  const int need = d.q - A.nslot + 1;
-  Spin sp = spin_start();
-  while (lds_ld_acq(&c->freed[slot]) < need)
-    if (!spin_ok(A, c, sp)) return false;
-  char* dst = ring + (size_t)slot * kChunkBytes + lane * 16;
-#pragma unroll
-  for (int j = 0; j < kWaveLoads; ++j) lds_st16(dst + j * 1024, r[j]);
-  if (lane == 0) lds_st_rel(&c->ready[slot], d.q + 1);
+  if (A->trace) wait_ticks += now_ticks() - t0;
   return true;
 }
 
-__device__ void loader_main(const DevArgs& A, char* ring, Ctrl* c, int cu, int lw, int lane) {
-  const Task* T = A.tasks + A.task_off[cu];
-  const int rpc = 4096 / A.hd;
-  LoaderIter it{0, A.task_off[cu + 1] - A.task_off[cu], 0, 0, 0, lw};
-  LDesc da, db;
-  u32x4 ra[kWaveLoads], rb[kWaveLoads];
-  bool have_a = loader_next(A, T, c, cu, rpc, it, da);
-  if (have_a) issue_loads(A, T, c, cu, da, lane, ra);
-  while (have_a) {
-    bool have_b = loader_next(A, T, c, cu, rpc, it, db);
-    if (have_b) issue_loads(A, T, c, cu, db, lane, rb);
-    if (!store_chunk(A, ring, c, da, lane, ra)) return;
-    if (!have_b) break;
-    have_a = loader_next(A, T, c, cu, rpc, it, da);
-    if (have_a) issue_loads(A, T, c, cu, da, lane, ra);
-    if (!store_chunk(A, ring, c, db, lane, rb)) return;
+// Ring bookkeeping of one loader wave: chunk q goes to slot q % nslot; the
+// chunk issued last is published (ready = q + 1) once its loads landed.
+struct LoaderRing {
+  int q;          // next chunk sequence number of this loader
+  int slot;       // q % nslot
+  int prev_slot;  // slot of the issued, not yet published chunk (-1 none)
+  int prev_q;
+  uint64_t wfull;
+};
+
+__device__ __forceinline__ bool ring_acquire(DArgs A, Ctrl* c, LoaderRing& R, int lane) {
+  const int need = R.q - A->nslot + 1;
+  if (lds_flag_read(&c->freed[R.slot]) < need) {
+    // about to block: publish the chunk still in flight first, so that a
+    // landed chunk never waits behind a free slot
+    if (R.prev_slot >= 0) {
+      wait_vmcnt0();
+      if (lane == 0) lds_flag_write(&c->ready[R.prev_slot], R.prev_q + 1);
+      R.prev_slot = -1;
+    }
+    if (!loader_wait_free(A, c, R.slot, need, R.wfull)) return false;
+  }
+  return true;
+}
+__device__ __forceinline__ void ring_issued(DArgs A, Ctrl* c, LoaderRing& R, int lane) {
+  if (R.prev_slot >= 0) {
+    wait_vmcnt16();  // the previous chunk's 16 loads have landed in LDS
+    if (lane == 0) lds_flag_write(&c->ready[R.prev_slot], R.prev_q + 1);
+  }
+  R.prev_slot = R.slot;
+  R.prev_q = R.q;
+  R.q += kLoaderWaves;
+  R.slot += kLoaderWaves;
+  while (R.slot >= A->nslot) R.slot -= A->nslot;
+}
+
+__device__ void loader_main(DArgs A, char* ring, Ctrl* c, int cu, int lw, int lane) {
+  A = uni(A);
+  const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
+  const int nt = as_const(A->task_off)[cu + 1] - as_const(A->task_off)[cu];
+  const int rpc = 4096 / A->hd;
+  // per-sequence lengths into registers before any load is in flight
+  SeqLens sl;
+#pragma unroll
+  for (int i = 0; i < kMaxBatch; ++i) sl.v[i] = i < A->b ? c->slen[i] : 1;
+  const uint64_t t_start = A->trace ? now_ticks() : 0;
+  LoaderRing R{lw, lw % A->nslot, -1, 0, 0};
+  int qbase = 0;
+  for (int ti = 0; ti < nt; ++ti) {
+    const Task t = load_task(uni(T + ti));
+    if (t.type == TT_GEMV) {
+      const int nch = t.nchunks;
+      int local = R.q - qbase;
+      if (local < nch) {
+        int sub = local % t.nsub, kb = t.k0 / kKBlock + local / t.nsub;
+        RowBase rb = sub_rows(A, t, sub);
+        while (local < nch) {
+          if (!ring_acquire(A, c, R, lane)) return;
+          dma_gemv_chunk(A, rb, kb, t.k1, lane, ring + (size_t)R.slot * kChunkBytes);
+          ring_issued(A, c, R, lane);
+          local += kLoaderWaves;
+          const int old_sub = sub;
+          sub += kLoaderWaves;
+          while (sub >= t.nsub) {
+            sub -= t.nsub;
+            ++kb;
+          }
+          if (sub != old_sub) rb = sub_rows(A, t, sub);
+        }
+      }
+      qbase += nch;
+    } else if (t.type == TT_ATTN) {
+      const long long W = attn_total_r(sl, A->b, A->nkv);
+      long long pos = cu_lo(cu, W, A->ncu);
+      const long long hi = cu_lo(cu + 1, W, A->ncu);
+      Piece P;
+      int pbase = qbase;
+      while (next_piece_r(sl, A->b, A->nkv, rpc, pos, hi, P)) {
+        const size_t head = (((size_t)t.layer * A->kv_bcap + P.i) * A->nkv + P.g) * A->kv_scap;
+        for (int ch = R.q - pbase; ch < P.nch; ch += kLoaderWaves) {
+          if (!ring_acquire(A, c, R, lane)) return;
+          const size_t row0 = (head + P.j0 + (size_t)ch * rpc) * A->hd;
+          const int rows = min(rpc, P.ncached - ch * rpc);
+          char* dst = ring + (size_t)R.slot * kChunkBytes;
+          if (A->hd == 128) dma_attn_chunk<128>(A, A->kc + row0, A->vc + row0, rows, lane, dst);
+          else dma_attn_chunk<64>(A, A->kc + row0, A->vc + row0, rows, lane, dst);
+          ring_issued(A, c, R, lane);
+        }
+        pbase += P.nch;
+      }
+      qbase = pbase;
+    }
+  }
+  if (R.prev_slot >= 0) {
+    wait_vmcnt0();
+    if (lane == 0) lds_flag_write(&c->ready[R.prev_slot], R.prev_q + 1);
+  }
+  if (A->trace && lane == 0) {
+    uint64_t* st = A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * 32;
+    st[lw] = R.wfull;
+    if (lw == 0) st[13] = now_ticks() - t_start;
   }
 }
 
 // ================================================================ compute
+__device__ int attn_task_chunks(DArgs A, const Ctrl* c, int cu, int rpc) {
+  A = uni(A);
+  long long W = attn_total(c, A->b, A->nkv);
+  long long pos = cu_lo(cu, W, A->ncu), hi = cu_lo(cu + 1, W, A->ncu);
+  Piece P;
+  int n = 0;
+  while (next_piece(c, A->b, A->nkv, rpc, pos, hi, P)) n += P.nch;
+  return n;
+}
 struct CState {
+  uint64_t t_stream;  // trace: when the task's last chunk was consumed
+  uint64_t w_empty;   // trace: ticks spent waiting for the loader
+  uint64_t w_bar;     // trace: ticks spent in compute barriers
+  uint64_t t_math;    // trace: ticks spent on chunk math
+  uint64_t t_stage;   // trace: ticks spent staging GEMV inputs
+  uint64_t t_epi;     // trace: ticks spent in reductions and epilogues
   int gen;      // compute-barrier generation
   int q;        // chunk sequence number of the current task's first chunk
   int last_dep; // counter of the last dependency already satisfied
   int x_stage, x_layer, x_k0, x_k1;  // signature of the staged input slice
+  int r_stage, r_layer;              // stage whose RMS scales are in Ctrl::rms
 };
 
-__device__ __forceinline__ bool wait_chunk(const DevArgs& A, Ctrl* c, int gq) {
-  const int slot = gq % A.nslot;
+__device__ __forceinline__ bool wait_chunk(DArgs A, Ctrl* c, int gq, uint64_t& wait_ticks) {
+  const int slot = gq % A->nslot;
+  if (lds_ld_acq(&c->ready[slot]) >= gq + 1) return true;
   Spin sp = spin_start();
   while (lds_ld_acq(&c->ready[slot]) < gq + 1)
     if (!spin_ok(A, c, sp)) return false;
+  if (A->trace) wait_ticks += now_ticks() - sp.t0;
   return true;
 }
-__device__ __forceinline__ void free_chunk(const DevArgs& A, Ctrl* c, int gq, int lane) {
-  if (lane == 0) lds_st_rel(&c->freed[gq % A.nslot], gq + 1);
+__device__ __forceinline__ void free_chunk(DArgs A, Ctrl* c, int gq, int lane) {
+  if (lane == 0) lds_st_rel(&c->freed[gq % A->nslot], gq + 1);
 }
 
 // Wave-wide sum over 16-lane groups (lanes l, l^1, ..., l^8).
@@ -464,43 +683,50 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
   return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)idx);
 }
 
-// ---- stage the GEMV input slice x[n][k0:k1] (bf16) into LDS, and the RMS
-//      scales of the stages that normalize their input.
-__device__ bool stage_input(const DevArgs& A, const Task& t, char* xb, Ctrl* c, CState& s, int w, int lane) {
-  if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == t.k0 && s.x_k1 == t.k1) return true;
+// ---- stage the GEMV input slice x[n][kk0:kk1) (bf16, n < b) into LDS with
+//      rows padded to kk1-kk0+8 elements, and the RMS scales of stages that
+//      normalize their input.  Skipped when the same slice is already staged.
+__device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int kk1, char* xb, Ctrl* c, CState& s, int w,
+                            int lane) {
+  if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == kk0 && s.x_k1 == kk1) return true;
+  // every compute wave must be done reading the previous slice
+  if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   const int K = stage_K(A, t.stage);
-  const int ksl = t.k1 - t.k0, ksp = ksl + 8;
+  const int ksl = kk1 - kk0, ksp = ksl + 8;
   const uint16_t* x = stage_x(A, t.stage, t.layer);
   const int per_row = ksl / 8;
-  const int units = A.b * per_row;
+  const int units = A->b * per_row;
   const int tid = w * 64 + lane;
   for (int u = tid; u < units; u += kComputeThreads) {
     int n = u / per_row, kq = u - n * per_row;
-    u32x4 v = co_load16(x, (uint32_t)(((size_t)n * K + t.k0 + 8 * kq) * 2));
+    u32x4 v = co_load16(x, (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 2));
     lds_st16(xb + ((size_t)n * ksp + 8 * kq) * 2, v);
   }
   const float* ss = stage_ss(A, t.stage, t.layer);
-  if (ss) {
-    const int nt = A.d / 16;
-    for (int n = w; n < A.b; n += kComputeWaves) {
+  if (ss && !(s.r_stage == t.stage && s.r_layer == t.layer)) {
+    const int nt = A->d / 16;
+    for (int n = w; n < A->b; n += kComputeWaves) {
       float acc = 0.f;
-      for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A.bcap + n) * 4));
+      for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4));
       for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-      if (lane == 0) c->rms[n] = 1.0f / sqrtf(acc / (float)A.d + A.eps);
+      if (lane == 0) c->rms[n] = 1.0f / sqrtf(acc / (float)A->d + A->eps);
     }
+    s.r_stage = t.stage;
+    s.r_layer = t.layer;
   }
   s.x_stage = t.stage;
   s.x_layer = t.layer;
-  s.x_k0 = t.k0;
-  s.x_k1 = t.k1;
-  return cbar(A, c, s.gen, lane);
+  s.x_k0 = kk0;
+  s.x_k1 = kk1;
+  return cbar(A, c, s.gen, lane, &s.w_bar);
 }
 
 // ---- VALU chunk: 16 rows x 512 K; lane l covers K elements [8l, 8l+8)
 template <int NB>
-__device__ __forceinline__ void valu_chunk(const char* slot, const char* xb, int ksp, int kl, int lane, float (&acc)[16][NB]) {
+__device__ __forceinline__ void valu_chunk(const char* slot, const char* xb, int ksp, int kl, int klen, int lane,
+                                           float (&acc)[16][NB]) {
   u32x4 xv[NB];
-  const bool ok = kl < ksp - 8;  // inside the slice (ksp = slice + 8)
+  const bool ok = kl < klen;
 #pragma unroll
   for (int n = 0; n < NB; ++n) xv[n] = ok ? lds_ld16(xb + ((size_t)n * ksp + kl) * 2) : u32x4{0, 0, 0, 0};
 #pragma unroll
@@ -548,57 +774,54 @@ __device__ __forceinline__ void valu_reduce(float (&acc)[16][NB], int lane, floa
   }
 }
 
-// ---- MFMA chunk: R sub-tiles x (16/R) k-steps of 32
-template <int R>
-__device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int ksp, int kstep0, int nsteps, int b, int lane, f32x4 (&acc)[R]) {
-  constexpr int SPC = kWaveLoads / R;
+// ---- MFMA chunk: one 16-row sub-tile x 16 k-steps of 32; B operand (the
+//      input, batch padded to 16 with zeros) from the staged LDS slice.
+__device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int ksp, int kl, int klen, int b, int lane,
+                                           f32x4& acc) {
   const int n = lane & 15, kq = 8 * (lane >> 4);
 #pragma unroll
-  for (int s = 0; s < SPC; ++s) {
-    if (kstep0 + s >= nsteps) break;
-    const int kl = 32 * (kstep0 + s) + kq;
-    u32x4 bv = n < b ? lds_ld16(xb + ((size_t)n * ksp + kl) * 2) : u32x4{0, 0, 0, 0};
-    bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bv);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      u32x4 av = lds_ld16(slot + (s * R + r) * 1024 + lane * 16);
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bb, acc[r], 0, 0, 0);
-    }
+  for (int s = 0; s < kWaveLoads; ++s) {
+    if (kl + 32 * s >= klen) break;
+    const int k = kl + 32 * s + kq;
+    u32x4 bv = n < b ? lds_ld16(xb + ((size_t)n * ksp + k) * 2) : u32x4{0, 0, 0, 0};
+    u32x4 av = lds_ld16(slot + s * 1024 + lane * 16);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
+                                                  acc, 0, 0, 0);
   }
 }
 
 // Epilogue of one output element (row `lr` of the stage, sequence n) of a
-// complete tile.  Threads map t -> (n = t >> 4, row = t & 15), so each
-// 16-lane group holds one sequence's 16 consecutive rows.
-__device__ void gemv_epilogue(const DevArgs& A, const Task& t, Ctrl* c, int r, int row, int n, float val, float val_up, int lane) {
+// complete sub-tile.  Lanes map to (row = lane & 15, n), so each 16-lane
+// group holds one sequence's 16 consecutive rows.  `resid` is the residual
+// prefetched for O / DOWN.
+__device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, int lr, int row, int n, float val, float val_up,
+                              float resid, int lane) {
   const int l = t.layer;
   const int M = stage_M(A, t.stage);
-  const int lr = t.row0 + 16 * r + row;
-  const bool valid = n < A.b && lr < M;
+  const bool valid = n < A->b && lr < M;
   switch (t.stage) {
     case ST_QKV:
-      if (valid) co_storef(A.qkv, (uint32_t)((((size_t)l * A.bcap + n) * A.nqkv + lr) * 4), c->rms[n] * val);
+      if (valid) co_storef(A->qkv, (uint32_t)((((size_t)l * A->bcap + n) * A->nqkv + lr) * 4), c->rms[n] * val);
       break;
     case ST_O:
     case ST_DOWN: {
       // h = residual + projection; also the next RMSNorm's input and its
       // per-16-row sum of squares.
       const bool down = t.stage == ST_DOWN;
-      const float* hin = down ? A.hmid + (size_t)l * A.bcap * A.d : A.hres + (size_t)l * A.bcap * A.d;
-      float* hout = down ? A.hres + (size_t)(l + 1) * A.bcap * A.d : A.hmid + (size_t)l * A.bcap * A.d;
-      uint16_t* xo = down ? A.xattn + (size_t)(l + 1) * A.bcap * A.d : A.xmlp + (size_t)l * A.bcap * A.d;
-      const uint16_t* nw = down ? (l + 1 < A.L ? A.layers[l + 1].attn_norm : A.final_norm) : A.layers[l].mlp_norm;
-      float* ssout = down ? A.ssattn + (size_t)(l + 1) * (A.d / 16) * A.bcap : A.ssmlp + (size_t)l * (A.d / 16) * A.bcap;
-      const uint32_t off = (uint32_t)(((size_t)n * A.d + lr) * 4);
-      float h = valid ? co_loadf(hin, off) + val : 0.f;
+      float* hout = down ? A->hres + (size_t)(l + 1) * A->bcap * A->d : A->hmid + (size_t)l * A->bcap * A->d;
+      uint16_t* xo = down ? A->xattn + (size_t)(l + 1) * A->bcap * A->d : A->xmlp + (size_t)l * A->bcap * A->d;
+      const uint16_t* nw = down ? (l + 1 < A->L ? as_const(A->layers)[l + 1].attn_norm : A->final_norm) : as_const(A->layers)[l].mlp_norm;
+      float* ssout = down ? A->ssattn + (size_t)(l + 1) * (A->d / 16) * A->bcap : A->ssmlp + (size_t)l * (A->d / 16) * A->bcap;
+      const uint32_t off = (uint32_t)(((size_t)n * A->d + lr) * 4);
+      float h = valid ? resid + val : 0.f;
       float xn = valid ? h * bf2f(nw[lr]) : 0.f;
       float xn_next = __shfl_down(xn, 1);
       if (valid) {
         co_storef(hout, off, h);
-        if ((row & 1) == 0) co_store4(xo, (uint32_t)(((size_t)n * A.d + lr) * 2), pack_bf2(xn, xn_next));
+        if ((row & 1) == 0) co_store4(xo, (uint32_t)(((size_t)n * A->d + lr) * 2), pack_bf2(xn, xn_next));
       }
       float ss = sum16(h * h);
-      if (valid && row == 0) co_storef(ssout, (uint32_t)((((size_t)lr >> 4) * A.bcap + n) * 4), ss);
+      if (valid && row == 0) co_storef(ssout, (uint32_t)((((size_t)lr >> 4) * A->bcap + n) * 4), ss);
       break;
     }
     case ST_GU: {
@@ -610,14 +833,14 @@ __device__ void gemv_epilogue(const DevArgs& A, const Task& t, Ctrl* c, int r, i
       }
       float a_next = __shfl_down(a, 1);
       if (valid && row < 8 && (row & 1) == 0) {
-        const int out = 8 * ((t.row0 >> 4) + r) + row;
-        co_store4(A.act, (uint32_t)((((size_t)l * A.bcap + n) * A.I + out) * 2), pack_bf2(a, a_next));
+        const int out = 8 * (lr >> 4) + row;
+        co_store4(A->act, (uint32_t)((((size_t)l * A->bcap + n) * A->I + out) * 2), pack_bf2(a, a_next));
       }
       break;
     }
     default: {  // LM head + greedy argmax
       float v = valid ? c->rms[n] * val : 0.f;
-      if (valid) A.logits[(size_t)n * A.V + lr] = v;
+      if (valid) A->logits[(size_t)n * A->V + lr] = v;
       unsigned long long key = valid ? argmax_key(v, lr) : 0ull;
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) {
@@ -625,145 +848,164 @@ __device__ void gemv_epilogue(const DevArgs& A, const Task& t, Ctrl* c, int r, i
                                (uint32_t)__shfl_xor((int)(uint32_t)key, m);
         key = o > key ? o : key;
       }
-      if (row == 0 && n < A.b && key) __hip_atomic_fetch_max(keys_ptr(A) + n, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (row == 0 && n < A->b && key) __hip_atomic_fetch_max(keys_ptr(A) + n, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
   }
 }
 
-template <int NB, int R>
-__device__ bool gemv_task(const DevArgs& A, const Task& t, char* ring, char* xb, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
-  if (!stage_input(A, t, xb, c, s, w, lane)) return false;
-  const int ksp = (t.k1 - t.k0) + 8;
-  // ---- stream the task's chunks (chunk q belongs to compute wave q % 4)
+// One GEMV task: a row group of nsub 16-row sub-tiles over K range [k0, k1).
+// Compute wave w owns sub-tile w: it consumes that sub-tile's chunks, reduces
+// across its own lanes and runs the epilogue, with no cross-wave reduction.
+// A group whose K range is split over several tasks publishes partials; the
+// last piece to finish sums them in piece order and runs the epilogue.
+template <int NB>
+__device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, Ctrl* c, CState& s, int cu,
+                          int w, int lane) {
+  A = uni(A);
+  const Task t = load_task(uni(tp));
+  const int nsub = t.nsub;
+  const bool own = w < nsub;
+  const int M = stage_M(A, t.stage);
+  const int kb0 = t.k0 / kKBlock, nkb = (t.k1 - t.k0 + kKBlock - 1) / kKBlock;
+  const int lr0 = t.row0 + 16 * w;  // first row of the owned sub-tile
+  const int row = lane & 15;
+  // residual of the owned rows, prefetched while the weights stream
+  float resid[4] = {0.f, 0.f, 0.f, 0.f};
+  if (own && (t.stage == ST_O || t.stage == ST_DOWN)) {
+    const float* hin = t.stage == ST_DOWN ? A->hmid + (size_t)t.layer * A->bcap * A->d : A->hres + (size_t)t.layer * A->bcap * A->d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = (lane >> 4) + 4 * j;
+      if (n < A->b && lr0 + row < M) resid[j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4));
+    }
+  }
   float vacc[16][NB];
-  f32x4 macc[R];
-  if (!A.mfma) {
+  f32x4 macc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int n = 0; n < NB; ++n) vacc[j][n] = 0.f;
-  } else {
-#pragma unroll
-    for (int r = 0; r < R; ++r) macc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int nsteps = (t.k1 - t.k0) / 32;
-  for (int local = 0; local < t.nchunks; ++local) {
-    const int gq = s.q + local;
-    if ((gq & (kComputeWaves - 1)) != w) continue;
-    if (!wait_chunk(A, c, gq)) return false;
-    const char* slot = ring + (size_t)(gq % A.nslot) * kChunkBytes;
-    if (!A.mfma) valu_chunk<NB>(slot, xb, ksp, kValuBlock * local + 8 * lane, lane, vacc);
-    else mfma_chunk<R>(slot, xb, ksp, local * (kWaveLoads / R), nsteps, A.b, lane, macc);
-    free_chunk(A, c, gq, lane);
-  }
-  // ---- per-wave partial sums -> LDS
-  float* rw = red + w * 1024;
-  if (!A.mfma) {
-    float tot[NB];
-    valu_reduce<NB>(vacc, lane, tot);
-    if ((lane & 3) == 0) {
-      const int row = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-#pragma unroll
-      for (int n = 0; n < NB; ++n) rw[row * 16 + n] = tot[n];
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < R; ++r) *(f32x4*)(rw + (r * 64 + lane) * 4) = macc[r];
-  }
-  if (!cbar(A, c, s.gen, lane)) return false;
-  // ---- combine the 4 waves; thread -> (n, row)
-  const int tid = w * 64 + lane, n = tid >> 4, row = tid & 15;
-  auto value = [&](int r, int rw_) -> float {
-    float v = 0.f;
-    if (!A.mfma) {
-#pragma unroll
-      for (int ww = 0; ww < kComputeWaves; ++ww) v += red[ww * 1024 + rw_ * 16 + n];
-    } else {
-      const int src = n + 16 * (rw_ >> 2), i = rw_ & 3;
-#pragma unroll
-      for (int ww = 0; ww < kComputeWaves; ++ww) v += red[ww * 1024 + (r * 64 + src) * 4 + i];
-    }
-    return v;
-  };
-  const int Rn = A.mfma ? R : 1;
-  float vals[R], ups[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    vals[r] = r < Rn ? value(r, row) : 0.f;
-    ups[r] = (r < Rn && t.stage == ST_GU && row < 8) ? value(r, row + 8) : 0.f;
-  }
-  if (t.nks > 1) {
-    // split-K: publish this slice's partial; the last slice of the group sums
-    // all partials in slice order and runs the epilogue.
-    float* pb = A.part + (size_t)(t.part_slot + t.ks) * 1024;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r < Rn) co_storef(pb, (uint32_t)((r * 256 + tid) * 4), vals[r]);
-    wait_mem();
-    if (!cbar(A, c, s.gen, lane)) return false;
-    if (w == 0) {
-      int fin = 0;
-      if (lane == 0) {
-        uint32_t* gc = A.grp_ctr + A.grp_off[t.stage] + t.group;
-        uint32_t old = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        fin = (int)old == t.nks - 1;
-        if (fin) __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lds_st_rel(&c->fin, fin);
+    for (int n = 0; n < NB; ++n) vacc[j][n] = 0.f;
+  // K windows that fit the LDS staging buffer
+  int wkb = ((A->xb_bytes / (2 * A->b)) - 8) / kKBlock;
+  if (wkb < 1) wkb = 1;
+  for (int wb = 0; wb < nkb; wb += wkb) {
+    const int we = min(nkb, wb + wkb);
+    const int kk0 = t.k0 + wb * kKBlock, kk1 = min(t.k1, t.k0 + we * kKBlock);
+    const uint64_t ts0 = A->trace ? now_ticks() : 0;
+    if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane)) return false;
+    if (A->trace) s.t_stage += now_ticks() - ts0;
+    const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0;
+    if (own) {
+      for (int kb = wb; kb < we; ++kb) {
+        const int gq = s.q + kb * nsub + w;
+        if (!wait_chunk(A, c, gq, s.w_empty)) return false;
+        const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
+        const int kl = (kb - wb) * kKBlock;
+        const uint64_t tm0 = A->trace ? now_ticks() : 0;
+        if (!A->mfma) valu_chunk<NB>(slot, xb, ksp, kl + 8 * lane, klen, lane, vacc);
+        else mfma_chunk(slot, xb, ksp, kl, klen, A->b, lane, macc);
+        free_chunk(A, c, gq, lane);
+        if (A->trace) s.t_math += now_ticks() - tm0;
       }
     }
-    if (!cbar(A, c, s.gen, lane)) return false;
-    if (lds_ld_acq(&c->fin)) {
-      const float* p0 = A.part + (size_t)t.part_slot * 1024;
+  }
+  (void)kb0;
+  const uint64_t te0 = A->trace ? now_ticks() : 0;
+  // owned sub-tile totals -> this wave's LDS scratch as [16 rows][16 n]
+  float* rw = red + w * 1024;
+  if (own) {
+    if (!A->mfma) {
+      float tot[NB];
+      valu_reduce<NB>(vacc, lane, tot);
+      if ((lane & 3) == 0) {
+        const int rr = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (r >= Rn) continue;
+        for (int n = 0; n < NB; ++n) rw[rr * 16 + n] = tot[n];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rw[(4 * (lane >> 4) + i) * 16 + (lane & 15)] = macc[i];
+    }
+  }
+  float val[4], up[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = (lane >> 4) + 4 * j;
+    val[j] = own ? rw[row * 16 + n] : 0.f;
+    up[j] = (own && t.stage == ST_GU && row < 8) ? rw[(row + 8) * 16 + n] : 0.f;
+  }
+  bool do_epi = own;
+  if (t.nks > 1) {
+    float* pb = A->part + (size_t)(t.part_slot + t.ks) * 1024 + w * 256;
+    if (own) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) co_storef(pb, (uint32_t)((((lane >> 4) + 4 * j) * 16 + row) * 4), val[j]);
+    }
+    wait_mem();
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    if (w == 0 && lane == 0) {
+      uint32_t* gc = A->grp_ctr + A->grp_off[t.stage] + t.group;
+      uint32_t old = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int fin = (int)old == t.nks - 1;
+      if (fin) __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_st_rel(&c->fin, fin);
+    }
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    const bool fin = lds_ld_acq(&c->fin) != 0;
+    do_epi = own && fin;
+    if (do_epi) {
+      const float* p0 = A->part + (size_t)t.part_slot * 1024 + w * 256;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = ((lane >> 4) + 4 * j) * 16 + row;
         float v = 0.f, u = 0.f;
         for (int k = 0; k < t.nks; ++k) {
-          v += co_loadf(p0, (uint32_t)(((size_t)k * 1024 + r * 256 + tid) * 4));
-          if (t.stage == ST_GU && row < 8) u += co_loadf(p0, (uint32_t)(((size_t)k * 1024 + r * 256 + tid + 8) * 4));
+          v += co_loadf(p0, (uint32_t)(((size_t)k * 1024 + e) * 4));
+          if (t.stage == ST_GU && row < 8) u += co_loadf(p0, (uint32_t)(((size_t)k * 1024 + e + 8) * 4));
         }
-        vals[r] = v;
-        ups[r] = u;
+        val[j] = v;
+        up[j] = u;
       }
-    } else {
-      wait_mem();
-      if (!cbar(A, c, s.gen, lane)) return false;
-      if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
-      return true;
     }
   }
+  if (do_epi) {
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (r < Rn) gemv_epilogue(A, t, c, r, row, n, vals[r], ups[r], lane);
-  wait_mem();
-  if (!cbar(A, c, s.gen, lane)) return false;
-  if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
+    for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[j], lane);
+  }
+  if (t.flags & kTaskSignal) {
+    wait_mem();
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
+  }
+  if (A->trace) s.t_epi += now_ticks() - te0;
   return true;
 }
 
 // ---- embedding gather: h0 = E[token] for 64 columns, plus the first
 //      RMSNorm's input and per-16-column sums of squares.
-__device__ bool embed_task(const DevArgs& A, const Task& t, Ctrl* c, CState& s, int cu, int w, int lane) {
+__device__ bool embed_task(DArgs A, TaskP tp, Ctrl* c, CState& s, int cu, int w, int lane) {
+  A = uni(A);
+  const Task t = load_task(uni(tp));
   const int tid = w * 64 + lane, n = tid >> 4, col = t.row0 + 4 * (tid & 15);
   float h[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool valid = n < A.b;
+  const bool valid = n < A->b;
   if (valid) {
-    const uint16_t* e = A.embed + (size_t)c->tok[n] * A.d + col;
+    const uint16_t* e = A->embed + (size_t)c->tok[n] * A->d + col;
     u32x2 ev = *(const u32x2*)e;
     h[0] = bf_lo(ev.x); h[1] = bf_hi(ev.x); h[2] = bf_lo(ev.y); h[3] = bf_hi(ev.y);
-    const uint16_t* nw = A.layers[0].attn_norm + col;
-    co_store16(A.hres, (uint32_t)(((size_t)n * A.d + col) * 4),
+    const uint16_t* nw = as_const(A->layers)[0].attn_norm + col;
+    co_store16(A->hres, (uint32_t)(((size_t)n * A->d + col) * 4),
                u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
-    co_store8(A.xattn, (uint32_t)(((size_t)n * A.d + col) * 2),
+    co_store8(A->xattn, (uint32_t)(((size_t)n * A->d + col) * 2),
               u32x2{pack_bf2(h[0] * bf2f(nw[0]), h[1] * bf2f(nw[1])), pack_bf2(h[2] * bf2f(nw[2]), h[3] * bf2f(nw[3]))});
   }
   float ss = h[0] * h[0] + h[1] * h[1] + h[2] * h[2] + h[3] * h[3];
   ss += __shfl_xor(ss, 1);
   ss += __shfl_xor(ss, 2);
-  if (valid && (tid & 3) == 0) co_storef(A.ssattn, (uint32_t)((((size_t)col >> 4) * A.bcap + n) * 4), ss);
+  if (valid && (tid & 3) == 0) co_storef(A->ssattn, (uint32_t)((((size_t)col >> 4) * A->bcap + n) * 4), ss);
   wait_mem();
-  if (!cbar(A, c, s.gen, lane)) return false;
+  if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   return true;
 }
@@ -776,7 +1018,7 @@ struct SoftState {
 // Load a head's 8 own elements and the 8 rotate-half partners of a raw q/k
 // row (fp32 in the qkv buffer), apply the optional per-head RMSNorm and RoPE.
 template <int HD>
-__device__ __forceinline__ void rope_head(const DevArgs& A, const float* src /* head base */, const uint16_t* normw, int p, int e0, float* out) {
+__device__ __forceinline__ void rope_head(DArgs A, const float* src /* head base */, const uint16_t* normw, int p, int e0, float* out) {
   constexpr int LPR = HD / 8;
   u32x4 a0 = co_load16(src, (uint32_t)(e0 * 4)), a1 = co_load16(src, (uint32_t)((e0 + 4) * 4));
   const int pe = (e0 + HD / 2) % HD;
@@ -791,7 +1033,7 @@ __device__ __forceinline__ void rope_head(const DevArgs& A, const float* src /* 
     for (int u = 0; u < 8; ++u) ss += x[u] * x[u];
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
-    const float rs = 1.0f / sqrtf(ss / (float)HD + A.eps);
+    const float rs = 1.0f / sqrtf(ss / (float)HD + A->eps);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       x[u] = x[u] * rs * bf2f(normw[e0 + u]);
@@ -800,7 +1042,7 @@ __device__ __forceinline__ void rope_head(const DevArgs& A, const float* src /* 
   }
   const bool first = e0 < HD / 2;
   const int fi = first ? e0 : e0 - HD / 2;
-  const float* cs = A.rope + ((size_t)p * (HD / 2) + fi) * 2;
+  const float* cs = A->rope + ((size_t)p * (HD / 2) + fi) * 2;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     float cv = cs[2 * u], sv = cs[2 * u + 1];
@@ -809,20 +1051,22 @@ __device__ __forceinline__ void rope_head(const DevArgs& A, const float* src /* 
 }
 
 template <int HD, int GM>
-__device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
+__device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
+  A = uni(A);
+  const Task t = load_task(uni(tp));
   constexpr int LPR = HD / 8, RP = 64 / LPR, RPC = 4096 / HD;
   constexpr float kLog2e = 1.4426950408889634f;
-  const int l = t.layer, G = A.G, e0 = (lane % LPR) * 8, gi = lane / LPR;
+  const int l = t.layer, G = A->G, e0 = (lane % LPR) * 8, gi = lane / LPR;
   const float qscale = kLog2e / sqrtf((float)HD);
-  const long long W = attn_total(c, A.b, A.nkv);
-  long long pos = cu_lo(cu, W, A.ncu), hi = cu_lo(cu + 1, W, A.ncu);
+  const long long W = attn_total(c, A->b, A->nkv);
+  long long pos = cu_lo(cu, W, A->ncu), hi = cu_lo(cu + 1, W, A->ncu);
   Piece P;
   int qc = s.q, pidx = 0;
-  const LayerW& lw = A.layers[l];
+  const MK_AS4 LayerW& lw = as_const(A->layers)[l];
   const int stride_st = kComputeWaves * GM * (HD + 4);
-  while (next_piece(c, A.b, A.nkv, RPC, pos, hi, P)) {
+  while (next_piece(c, A->b, A->nkv, RPC, pos, hi, P)) {
     const int p = c->slen[P.i] - 1;
-    const float* qrow = A.qkv + ((size_t)l * A.bcap + P.i) * A.nqkv;
+    const float* qrow = A->qkv + ((size_t)l * A->bcap + P.i) * A->nqkv;
     float q[GM][8], o[GM][8];
     SoftState st[GM];
 #pragma unroll
@@ -832,7 +1076,7 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
 #pragma unroll
       for (int u = 0; u < 8; ++u) o[h][u] = 0.f;
       if (h < G) {
-        rope_head<HD>(A, qrow + (size_t)(P.g * G + h) * HD, A.qk_norm ? lw.q_norm : nullptr, p, e0, q[h]);
+        rope_head<HD>(A, qrow + (size_t)(P.g * G + h) * HD, A->qk_norm ? lw.q_norm : nullptr, p, e0, q[h]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) q[h][u] *= qscale;
       } else {
@@ -844,8 +1088,8 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
     for (int ch = 0; ch < P.nch; ++ch) {
       const int gq = qc + ch;
       if ((gq & (kComputeWaves - 1)) != w) continue;
-      if (!wait_chunk(A, c, gq)) return false;
-      const char* slot = ring + (size_t)(gq % A.nslot) * kChunkBytes;
+      if (!wait_chunk(A, c, gq, s.w_empty)) return false;
+      const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
       const int rows = min(RPC, P.ncached - ch * RPC);
 #pragma unroll 2
       for (int pass = 0; pass < RPC / RP; ++pass) {
@@ -879,9 +1123,9 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
     // written to the cache and absorbed by lane group 0 of wave 0
     if (w == 0 && P.has_new) {
       float kn[8], vn[8];
-      const float* krow = qrow + A.qdim + (size_t)P.g * HD;
-      const float* vrow = qrow + A.qdim + A.kvdim + (size_t)P.g * HD;
-      rope_head<HD>(A, krow, A.qk_norm ? lw.k_norm : nullptr, p, e0, kn);
+      const float* krow = qrow + A->qdim + (size_t)P.g * HD;
+      const float* vrow = qrow + A->qdim + A->kvdim + (size_t)P.g * HD;
+      rope_head<HD>(A, krow, A->qk_norm ? lw.k_norm : nullptr, p, e0, kn);
       u32x4 v0 = co_load16(vrow, (uint32_t)(e0 * 4)), v1 = co_load16(vrow, (uint32_t)((e0 + 4) * 4));
       float vr[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
                      __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
@@ -890,9 +1134,9 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
       unpack8(kb, kn);
       unpack8(vb, vn);
       if (gi == 0) {
-        const size_t slot_row = ((((size_t)l * A.kv_bcap + P.i) * A.nkv + P.g) * A.kv_scap + p) * HD + e0;
-        *(u32x4*)(A.kc + slot_row) = kb;
-        *(u32x4*)(A.vc + slot_row) = vb;
+        const size_t slot_row = ((((size_t)l * A->kv_bcap + P.i) * A->nkv + P.g) * A->kv_scap + p) * HD + e0;
+        *(u32x4*)(A->kc + slot_row) = kb;
+        *(u32x4*)(A->vc + slot_row) = vb;
       }
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
@@ -942,7 +1186,7 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
         }
       }
     }
-    if (!cbar(A, c, s.gen, lane)) return false;
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     if (w == 0) {
       // merge the 4 wave states (lane group 0 holds 8 elements per lane)
       const float* s0 = red + (pidx & 1) * stride_st;
@@ -967,14 +1211,14 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
         }
       }
       const int s_i = c->slen[P.i];
-      const int c_first = cu_of(P.seg_start, W, A.ncu), c_last = cu_of(P.seg_start + s_i - 1, W, A.ncu);
+      const int c_first = cu_of(P.seg_start, W, A->ncu), c_last = cu_of(P.seg_start + s_i - 1, W, A->ncu);
       // CUs whose range is empty (fewer rows than CUs) hold no piece
-      const int npieces = W >= A.ncu ? c_last - c_first + 1
-                                     : (int)(cu_lo(c_last + 1, W, A.ncu) - cu_lo(c_first, W, A.ncu));
+      const int npieces = W >= A->ncu ? c_last - c_first + 1
+                                     : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
       bool finisher = npieces == 1;
       const int pstride = GM * (HD + 4);
       if (!finisher) {
-        float* dst = A.apart + (size_t)(cu + P.sid) * pstride;
+        float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
         if (gi == 0) {
 #pragma unroll
           for (int h = 0; h < GM; ++h) {
@@ -988,38 +1232,73 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
         }
         wait_mem();
         uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(A.seg_ctr + P.sid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) old = __hip_atomic_fetch_add(A->seg_ctr + P.sid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
         finisher = (int)old == npieces - 1;
         if (finisher) {
-          if (lane == 0) __hip_atomic_store(A.seg_ctr + P.sid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) __hip_atomic_store(A->seg_ctr + P.sid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // merge every piece of the segment, in piece order: (1) the
+          // per-head maximum over pieces, one piece per lane; (2) the
+          // weighted sums, one piece per lane group, then across groups.
+          auto piece_cu = [&](int pc) -> int {
+            return W >= A->ncu ? c_first + pc : cu_of(P.seg_start + pc, W, A->ncu);
+          };
+#pragma unroll
+          for (int h = 0; h < GM; ++h) M[h] = -INFINITY;
+          for (int p0 = 0; p0 < npieces; p0 += 64) {
+            const int pc = p0 + lane;
+            const float* src = A->apart + (size_t)(piece_cu(pc < npieces ? pc : 0) + P.sid) * pstride;
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+              if (h >= G) continue;
+              float mv = pc < npieces ? co_loadf(src, (uint32_t)((h * (HD + 4) + HD) * 4)) : -INFINITY;
+#pragma unroll
+              for (int m = 32; m >= 1; m >>= 1) mv = fmaxf(mv, __shfl_xor(mv, m));
+              M[h] = fmaxf(M[h], mv);
+            }
+          }
 #pragma unroll
           for (int h = 0; h < GM; ++h) {
-            M[h] = -INFINITY;
             Lsum[h] = 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) O[h][u] = 0.f;
-            if (h >= G) continue;
-            for (int cc = c_first; cc <= c_last; ++cc) {
-              if (W < A.ncu && cu_lo(cc + 1, W, A.ncu) == cu_lo(cc, W, A.ncu)) continue;
-              const float* src = A.apart + (size_t)(cc + P.sid) * pstride + h * (HD + 4);
-              u32x4 a0 = co_load16(src, (uint32_t)(e0 * 4)), a1 = co_load16(src, (uint32_t)((e0 + 4) * 4));
-              const float m2 = co_loadf(src, HD * 4), l2 = co_loadf(src, (HD + 1) * 4);
-              const float mn = fmaxf(M[h], m2);
-              const float fa = mn == -INFINITY ? 0.f : exp2f(M[h] - mn);
-              const float fb = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
-              float ov[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
-                             __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
+          }
+          constexpr int PPW = 64 / LPR;  // pieces per pass
+#pragma unroll 2
+          for (int p0 = 0; p0 < npieces; p0 += PPW) {
+            const int pc = p0 + gi;
+            if (pc < npieces) {
+              const float* src = A->apart + (size_t)(piece_cu(pc) + P.sid) * pstride;
 #pragma unroll
-              for (int u = 0; u < 8; ++u) O[h][u] = O[h][u] * fa + ov[u] * fb;
-              Lsum[h] = Lsum[h] * fa + l2 * fb;
-              M[h] = mn;
+              for (int h = 0; h < GM; ++h) {
+                if (h >= G) continue;
+                u32x4 a0 = co_load16(src, (uint32_t)((h * (HD + 4) + e0) * 4));
+                u32x4 a1 = co_load16(src, (uint32_t)((h * (HD + 4) + e0 + 4) * 4));
+                const float m2 = co_loadf(src, (uint32_t)((h * (HD + 4) + HD) * 4));
+                const float l2 = co_loadf(src, (uint32_t)((h * (HD + 4) + HD + 1) * 4));
+                const float f = M[h] == -INFINITY ? 0.f : exp2f(m2 - M[h]);
+                float ov[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
+                               __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) O[h][u] += f * ov[u];
+                Lsum[h] += f * l2;
+              }
+            }
+          }
+#pragma unroll
+          for (int msk = LPR; msk < 64; msk <<= 1) {
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+              if (h >= G) continue;
+#pragma unroll
+              for (int u = 0; u < 8; ++u) O[h][u] += __shfl_xor(O[h][u], msk);
+              Lsum[h] += __shfl_xor(Lsum[h], msk);
             }
           }
         }
       }
       if (finisher && gi == 0) {
-        uint16_t* ob = A.attn_out + ((size_t)l * A.bcap + P.i) * A.qdim;
+        uint16_t* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim;
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
           if (h >= G) continue;
@@ -1034,44 +1313,48 @@ __device__ bool attn_task(const DevArgs& A, const Task& t, char* ring, float* re
     ++pidx;
   }
   wait_mem();
-  if (!cbar(A, c, s.gen, lane)) return false;
+  if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   return true;
 }
 
 template <int HD>
-__device__ __forceinline__ bool attn_dispatch(const DevArgs& A, const Task& t, char* ring, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
-  if (A.G <= 1) return attn_task<HD, 1>(A, t, ring, red, c, s, cu, w, lane);
-  if (A.G <= 2) return attn_task<HD, 2>(A, t, ring, red, c, s, cu, w, lane);
-  if (A.G <= 4) return attn_task<HD, 4>(A, t, ring, red, c, s, cu, w, lane);
-  return attn_task<HD, 8>(A, t, ring, red, c, s, cu, w, lane);
+__device__ bool attn_dispatch(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
+  A = uni(A);
+  if (A->G <= 1) return attn_task<HD, 1>(A, tp, ring, red, c, s, cu, w, lane);
+  if (A->G <= 2) return attn_task<HD, 2>(A, tp, ring, red, c, s, cu, w, lane);
+  if (A->G <= 4) return attn_task<HD, 4>(A, tp, ring, red, c, s, cu, w, lane);
+  if constexpr (HD == 64) return attn_task<HD, 8>(A, tp, ring, red, c, s, cu, w, lane);
+  return false;  // group > 4 at head_dim 128 is rejected at mk_create
 }
 
-__device__ bool gemv_dispatch(const DevArgs& A, const Task& t, char* ring, char* xb, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
-  if (A.mfma) {
-    if (t.nsub == 4) return gemv_task<1, 4>(A, t, ring, xb, red, c, s, cu, w, lane);
-    if (t.nsub == 2) return gemv_task<1, 2>(A, t, ring, xb, red, c, s, cu, w, lane);
-    return gemv_task<1, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-  }
-  switch (A.b) {
-    case 1: return gemv_task<1, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-    case 2: return gemv_task<2, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-    case 3: return gemv_task<3, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-    case 4: return gemv_task<4, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-    case 5: return gemv_task<5, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-    case 6: return gemv_task<6, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
-    default: return gemv_task<7, 1>(A, t, ring, xb, red, c, s, cu, w, lane);
+__device__ bool gemv_dispatch(DArgs A, TaskP tp, char* ring, char* xb, float* red, Ctrl* c, CState& s, int cu,
+                              int w, int lane) {
+  A = uni(A);
+  if (A->mfma) return gemv_task<1>(A, tp, ring, xb, red, c, s, cu, w, lane);
+  switch (A->b) {
+    case 1: return gemv_task<1>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    case 2: return gemv_task<2>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    case 3: return gemv_task<3>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    case 4: return gemv_task<4>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    case 5: return gemv_task<5>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    case 6: return gemv_task<6>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    default: return gemv_task<7>(A, tp, ring, xb, red, c, s, cu, w, lane);
   }
 }
 
-__device__ void compute_main(const DevArgs& A, char* ring, char* xb, float* red, Ctrl* c, int cu, int w, int lane) {
-  const Task* T = A.tasks + A.task_off[cu];
-  const int nt = A.task_off[cu + 1] - A.task_off[cu];
-  CState s{0, 0, -1, -1, -1, -1, -1};
-  const int rpc = 4096 / A.hd;
+__device__ void compute_main(DArgs A, char* ring, char* xb, float* red, Ctrl* c, int cu, int w, int lane) {
+  A = uni(A);
+  const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
+  const int nt = as_const(A->task_off)[cu + 1] - as_const(A->task_off)[cu];
+  CState s{0, 0, 0, 0, 0, 0, 0, 0, -1, -1, -1, -1, -1, -1, -1};
+  const uint64_t t_kernel0 = A->trace ? now_ticks() : 0;
+  uint64_t* tr = (A->trace && w == 0 && lane == 0) ? A->trace + (size_t)cu * A->trace_cap * 4 : nullptr;
+  const int rpc = 4096 / A->hd;
   bool had_lm = false;
   for (int ti = 0; ti < nt; ++ti) {
-    const Task t = T[ti];
+    const Task t = load_task(uni(T + ti));
+    const uint64_t t_begin = tr ? now_ticks() : 0;
     if (t.wait_ctr >= 0 && t.wait_ctr != s.last_dep) {
       if (w == 0) {
         if (!wait_counter(A, c, t.wait_ctr, lane)) return;
@@ -1083,51 +1366,70 @@ __device__ void compute_main(const DevArgs& A, char* ring, char* xb, float* red,
       }
       s.last_dep = t.wait_ctr;
     }
+    const uint64_t t_dep = tr ? now_ticks() : 0;
+    s.t_stream = 0;
     bool ok;
     int nch = 0;
     if (t.type == TT_GEMV) {
-      ok = gemv_dispatch(A, t, ring, xb, red, c, s, cu, w, lane);
+      ok = gemv_dispatch(A, T + ti, ring, xb, red, c, s, cu, w, lane);
       nch = t.nchunks;
       had_lm = had_lm || t.stage == ST_LM;
     } else if (t.type == TT_ATTN) {
-      ok = A.hd == 128 ? attn_dispatch<128>(A, t, ring, red, c, s, cu, w, lane)
-                       : attn_dispatch<64>(A, t, ring, red, c, s, cu, w, lane);
+      ok = A->hd == 128 ? attn_dispatch<128>(A, T + ti, ring, red, c, s, cu, w, lane)
+                        : attn_dispatch<64>(A, T + ti, ring, red, c, s, cu, w, lane);
       nch = attn_task_chunks(A, c, cu, rpc);
     } else {
-      ok = embed_task(A, t, c, s, cu, w, lane);
+      ok = embed_task(A, T + ti, c, s, cu, w, lane);
     }
     if (!ok) return;
     s.q += nch;
+    if (tr && ti < A->trace_cap) {
+      tr[ti * 4 + 0] = ((uint64_t)ti << 32) | ((uint64_t)t.type << 8) | (uint64_t)t.stage;
+      tr[ti * 4 + 1] = t_begin;
+      tr[ti * 4 + 2] = t_dep;
+      tr[ti * 4 + 3] = now_ticks();
+    }
+  }
+  if (A->trace && lane == 0) {
+    uint64_t* st = A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * 32;
+    st[4 + w] = s.w_empty;
+    st[8 + w] = s.w_bar;
+    st[16 + w] = s.t_math;
+    st[20 + w] = s.t_stage;
+    st[24 + w] = s.t_epi;
+    if (w == 0) st[12] = now_ticks() - t_kernel0;
   }
   // Greedy tokens: once every LM task has signalled, the argmax keys are
   // final.  Every CU that ran LM tasks checks once; the CU whose signal was
   // the last one is guaranteed to see completion (duplicates write the same
   // values).
-  if (w == 0 && had_lm && A.next_tokens) {
+  if (w == 0 && had_lm && A->next_tokens) {
     wait_mem();
-    const int ctr = ctr_lm(A.L);
-    const uint32_t* p = bank_ptr(A, A.bank) + lane * A.ctr_stride + ctr;
+    const int ctr = ctr_lm(A->L);
+    const uint32_t* p = bank_ptr(A, A->bank) + lane * A->ctr_stride + ctr;
     int v = (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__all(v >= A.expect[ctr * kShards + lane]) && lane < A.b) {
+    if (__all(v >= as_const(A->expect)[ctr * kShards + lane]) && lane < A->b) {
       unsigned long long key = __hip_atomic_load(keys_ptr(A) + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      A.next_tokens[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+      A->next_tokens[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs A) {
+__global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
+  (void)args;
+  DArgs A = (DArgs)__builtin_amdgcn_kernarg_segment_ptr();
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* ring = lds;
-  char* xb = lds + (size_t)A.nslot * kChunkBytes;
-  float* red = (float*)(xb + A.xb_bytes);
+  char* xb = lds + (size_t)A->nslot * kChunkBytes;
+  float* red = (float*)(xb + A->xb_bytes);
   Ctrl* c = (Ctrl*)((char*)red + kRedBytes);
   const int cu = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 
   // zero this CU's slice of the bank the next step will use
   {
-    uint32_t* nb = bank_ptr(A, A.bank ^ 1);
-    const int per = (A.bank_words + A.ncu - 1) / A.ncu;
-    const int lo = cu * per, hi = min(A.bank_words, lo + per);
+    uint32_t* nb = bank_ptr(A, A->bank ^ 1);
+    const int per = (A->bank_words + A->ncu - 1) / A->ncu;
+    const int lo = cu * per, hi = min(A->bank_words, lo + per);
     for (int i = lo + tid; i < hi; i += kThreads) nb[i] = 0u;
   }
   if (tid < kMaxSlots) {
@@ -1141,24 +1443,24 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs A) {
     c->abort = 0;
   }
   // per-sequence inputs, validated and clamped identically on every CU
-  if (tid < A.b) {
+  if (tid < A->b) {
     uint32_t st = 0;
-    int tok = A.tokens[tid];
-    if (tok < 0 || tok >= A.V) {
+    int tok = A->tokens[tid];
+    if (tok < 0 || tok >= A->V) {
       st |= 1u;
-      tok = tok < 0 ? 0 : A.V - 1;
+      tok = tok < 0 ? 0 : A->V - 1;
     }
-    int p = A.positions[tid];
-    const int cap = min(A.max_seq, A.kv_scap);
+    int p = A->positions[tid];
+    const int cap = min(A->max_seq, A->kv_scap);
     if (p < 0 || p >= cap) {
       st |= 2u;
       p = p < 0 ? 0 : cap - 1;
     }
-    if (A.seq_lens[tid] != A.positions[tid] + 1) st |= 4u;
+    if (A->seq_lens[tid] != A->positions[tid] + 1) st |= 4u;
     c->tok[tid] = tok;
     c->pos[tid] = p;
     c->slen[tid] = p + 1;
-    if (st && cu == 0) atomicOr(A.status, st);
+    if (st && cu == 0) atomicOr(A->status, st);
   }
   __syncthreads();
   if (w < kComputeWaves) compute_main(A, ring, xb, red, c, cu, w, lane);
@@ -1171,8 +1473,12 @@ size_t lds_bytes(int nslot, int xb_bytes) {
 
 hipError_t launch_step(const DevArgs& A, hipStream_t stream) {
   const size_t lds = lds_bytes(A.nslot, A.xb_bytes);
-  hipError_t e = hipFuncSetAttribute((const void*)mk_step_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+  static size_t lds_set = 0;
+  if (lds > lds_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)mk_step_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = lds;
+  }
   hipLaunchKernelGGL(mk_step_kernel, dim3(A.ncu), dim3(kThreads), lds, stream, A);
   return hipGetLastError();
 }

@@ -39,44 +39,34 @@ int stage_k(const PlanCfg& p, int st) {
   return 0;
 }
 
-// K-slice boundary i of nks, aligned to 64 elements.
-int kbound(int K, int nks, int i) {
-  if (i >= nks) return K;
-  long long u = (long long)(K / 64) * i / nks;
-  return (int)(u * 64);
-}
-
-struct Choice {
-  int R = 1, nks = 1;
-  double cost = 1e300;
+// A GEMV stage is a grid of columns: (row group of `gs` 16-row sub-tiles) x
+// (512-wide K block).  Columns are dealt to CUs as equal contiguous ranges
+// ("stream-K"): a CU's range is split into tasks at row-group boundaries, and
+// a row group whose K range is split over several CUs is finished by the
+// last of its pieces.
+struct Tiling {
+  int gs = 4;          // sub-tiles per group
+  int nkb = 1;         // K blocks
+  int ngroups = 1;
+  long long ncols = 1;
 };
 
-Choice choose_tiling(const PlanCfg& p, int M, int K, int batch, bool mfma) {
-  Choice best;
-  const int Rs_mfma[3] = {4, 2, 1};
-  const int Rs_valu[1] = {1};
-  const int* Rs = mfma ? Rs_mfma : Rs_valu;
-  int nR = mfma ? 3 : 1;
-  for (int ri = 0; ri < nR; ++ri) {
-    int R = Rs[ri];
-    long long groups = (M + 16 * R - 1) / (16 * R);
-    for (int nks = 1; nks <= 64; ++nks) {
-      if (K / nks < 64) break;
-      int kmax = 0;
-      for (int i = 0; i < nks; ++i) kmax = std::max(kmax, kbound(K, nks, i + 1) - kbound(K, nks, i));
-      if ((long long)batch * kmax * 2 > p.xb_bytes) continue;
-      long long units = groups * nks;
-      long long per_cu = (units + p.ncu - 1) / p.ncu;
-      // bytes streamed by the busiest CU plus a per-task overhead expressed in
-      // bytes (reduction, epilogue, signal); split-K adds a partial round trip.
-      double unit_bytes = 16.0 * R * kmax * 2.0;
-      double overhead = 12288.0 + (nks > 1 ? 16384.0 : 0.0);
-      double cost = per_cu * (unit_bytes + overhead);
-      if (cost < best.cost * 0.999) {
-        best.cost = cost;
-        best.R = R;
-        best.nks = nks;
-      }
+Tiling tile_stage(const PlanCfg& p, int M, int K) {
+  const int st = (M + 15) / 16, nkb = (K + kKBlock - 1) / kKBlock;
+  Tiling best;
+  double best_cost = 1e300;
+  for (int gs = kGroupSub; gs >= 1; gs >>= 1) {
+    Tiling t;
+    t.gs = gs;
+    t.nkb = nkb;
+    t.ngroups = (st + gs - 1) / gs;
+    t.ncols = (long long)t.ngroups * nkb;
+    // chunks streamed by the busiest CU, plus a small per-task charge
+    long long per_cu = (t.ncols + p.ncu - 1) / p.ncu;
+    double cost = (double)per_cu * gs + 0.25 * (double)per_cu / nkb + (gs < kGroupSub ? 0.01 : 0.0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = t;
     }
   }
   return best;
@@ -130,60 +120,94 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
       t.row0 = 64 * i;
       t.nsub = 64;
       t.signal_ctr = ctr_embed();
+      t.flags = kTaskSignal;
       S[owner(i, n, ncu)].push_back(t);
     }
   }
 
   // GEMV stages: choose a tiling per stage kind once (the same for all layers).
-  Choice ch[6];
+  Tiling tl[6];
   int grp_base[6] = {0, 0, 0, 0, 0, 0};
   int part_base[6] = {0, 0, 0, 0, 0, 0};
   const int gemv_stages[5] = {ST_QKV, ST_O, ST_GU, ST_DOWN, ST_LM};
+  // pieces of each group, identical for every layer of a stage
+  std::vector<std::vector<int>> group_pieces(6);
   for (int si = 0; si < 5; ++si) {
     int st = gemv_stages[si];
-    ch[st] = choose_tiling(pc, stage_rows(pc, st), stage_k(pc, st), batch, mfma);
-    int groups = (stage_rows(pc, st) + 16 * ch[st].R - 1) / (16 * ch[st].R);
-    if (ch[st].nks > 1) {
-      grp_base[st] = grp_counters;
-      grp_counters += groups;
-      part_base[st] = part_blocks;
-      part_blocks += groups * ch[st].nks;
+    tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st));
+    const Tiling& T = tl[st];
+    group_pieces[st].assign(T.ngroups, 0);
+    for (int c = 0; c < ncu; ++c) {
+      long long c0 = T.ncols * c / ncu, c1 = T.ncols * (c + 1) / ncu;
+      for (long long col = c0; col < c1;) {
+        int g = (int)(col / T.nkb);
+        long long gend = std::min(c1, (long long)(g + 1) * T.nkb);
+        group_pieces[st][g] += 1;
+        col = gend;
+      }
     }
-    P.stage_ksplit[st] = ch[st].nks;
-    P.stage_rows[st] = 16 * ch[st].R;
+    int split_groups = 0, split_pieces = 0;
+    for (int v : group_pieces[st])
+      if (v > 1) {
+        split_groups++;
+        split_pieces += v;
+      }
+    grp_base[st] = grp_counters;
+    grp_counters += T.ngroups;
+    part_base[st] = part_blocks;
+    part_blocks += split_pieces;
+    int maxp = 1;
+    for (int v : group_pieces[st]) maxp = std::max(maxp, v);
+    P.stage_ksplit[st] = maxp;
+    P.stage_rows[st] = 16 * T.gs;
+    (void)split_groups;
   }
   P.stage_ksplit[ST_ATTN] = 0;
   P.stage_rows[ST_ATTN] = 0;
+  // partial-block base of each split group (same layout for every layer)
+  std::vector<std::vector<int>> group_part(6);
+  for (int si = 0; si < 5; ++si) {
+    int st = gemv_stages[si];
+    group_part[st].assign(tl[st].ngroups, -1);
+    int nxt = part_base[st];
+    for (int g = 0; g < tl[st].ngroups; ++g)
+      if (group_pieces[st][g] > 1) {
+        group_part[st][g] = nxt;
+        nxt += group_pieces[st][g];
+      }
+  }
 
   auto emit_gemv = [&](int st, int layer, int wait, int signal) {
     const int M = stage_rows(pc, st), K = stage_k(pc, st);
-    const Choice& c = ch[st];
-    const long long groups = (M + 16 * c.R - 1) / (16 * c.R);
-    const long long units = groups * c.nks;
-    for (long long u = 0; u < units; ++u) {
-      int g = (int)(u / c.nks), ks = (int)(u % c.nks);
-      Task t = base_task(TT_GEMV, st, layer);
-      t.row0 = g * 16 * c.R;
-      t.nsub = c.R;
-      t.k0 = kbound(K, c.nks, ks);
-      t.k1 = kbound(K, c.nks, ks + 1);
-      t.ks = ks;
-      t.nks = c.nks;
-      t.group = c.nks > 1 ? g : -1;
-      t.part_slot = c.nks > 1 ? part_base[st] + g * c.nks : -1;
-      t.wait_ctr = wait;
-      t.signal_ctr = signal;
-      int ks_len = t.k1 - t.k0;
-      if (mfma) {
-        int steps = ks_len / 32;
-        t.nchunks = (steps * c.R + kWaveLoads - 1) / kWaveLoads;
-      } else {
-        t.nchunks = (ks_len + kValuBlock - 1) / kValuBlock;
+    const Tiling& T = tl[st];
+    const int nst = (M + 15) / 16;
+    std::vector<int> seen(T.ngroups, 0);
+    for (int c = 0; c < ncu; ++c) {
+      long long c0 = T.ncols * c / ncu, c1 = T.ncols * (c + 1) / ncu;
+      int first = (int)S[c].size();
+      for (long long col = c0; col < c1;) {
+        int g = (int)(col / T.nkb);
+        int kb_a = (int)(col - (long long)g * T.nkb);
+        long long gend = std::min(c1, (long long)(g + 1) * T.nkb);
+        int kb_b = (int)(gend - (long long)g * T.nkb);
+        Task t = base_task(TT_GEMV, st, layer);
+        t.row0 = g * 16 * T.gs;
+        t.nsub = std::min(T.gs, nst - g * T.gs);
+        t.k0 = kb_a * kKBlock;
+        t.k1 = std::min(K, kb_b * kKBlock);
+        t.nks = group_pieces[st][g];
+        t.ks = seen[g]++;
+        t.group = g;
+        t.part_slot = t.nks > 1 ? group_part[st][g] : -1;
+        t.wait_ctr = wait;
+        t.signal_ctr = signal;
+        t.nchunks = t.nsub * (kb_b - kb_a);
+        int rows = std::min(16 * t.nsub, M - t.row0);
+        cu_bytes[c] += (long long)rows * (t.k1 - t.k0) * 2;
+        S[c].push_back(t);
+        col = gend;
       }
-      int rows = std::min(16 * c.R, M - t.row0);
-      int cu = owner(u, units, ncu);
-      cu_bytes[cu] += (long long)rows * ks_len * 2;
-      S[cu].push_back(t);
+      if ((int)S[c].size() > first) S[c].back().flags |= kTaskSignal;
     }
   };
 
@@ -194,6 +218,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
       Task t = base_task(TT_ATTN, ST_ATTN, l);
       t.wait_ctr = ctr_stage(l, ST_QKV);
       t.signal_ctr = ctr_stage(l, ST_ATTN);
+      t.flags = kTaskSignal;
       S[c].push_back(t);
     }
     emit_gemv(ST_O, l, ctr_stage(l, ST_ATTN), ctr_stage(l, ST_O));
@@ -210,7 +235,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
     n_tasks += (int)S[c].size();
     max_tasks = std::max(max_tasks, (int)S[c].size());
     for (const Task& t : S[c]) {
-      if (t.signal_ctr >= 0) {
+      if (t.signal_ctr >= 0 && (t.flags & kTaskSignal)) {
         expect[(size_t)t.signal_ctr * kShards + (c % kShards)] += 1;
         total_signals[t.signal_ctr] += 1;
       }
@@ -218,27 +243,32 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   }
 
   // ---- validation --------------------------------------------------------
-  // (1) every (group, k-slice) unit of every GEMV stage exactly once, and
-  //     every staged input slice fits the LDS staging buffer.
+  // (1) every (row, K element) of every GEMV stage is covered exactly once,
+  //     the pieces of each group tile its K range in order, and chunk counts
+  //     match the tiling.
   for (int l = 0; l <= pc.L; ++l) {
     for (int si = 0; si < 5; ++si) {
       int st = gemv_stages[si];
       if ((st == ST_LM) != (l == pc.L)) continue;
-      const Choice& c = ch[st];
-      long long groups = (stage_rows(pc, st) + 16 * c.R - 1) / (16 * c.R);
-      std::vector<int> seen(groups * c.nks, 0);
+      const Tiling& T = tl[st];
+      const int M = stage_rows(pc, st), K = stage_k(pc, st);
+      std::vector<int> next_k(T.ngroups, 0), next_piece(T.ngroups, 0);
       long long covered = 0;
       for (int cu = 0; cu < ncu; ++cu)
         for (const Task& t : S[cu]) {
           if (t.type != TT_GEMV || t.stage != st || t.layer != l) continue;
-          long long g = t.row0 / (16 * c.R);
-          seen[g * c.nks + t.ks] += 1;
-          covered += (long long)std::min(16 * c.R, stage_rows(pc, st) - t.row0) * (t.k1 - t.k0);
-          if ((long long)batch * (t.k1 - t.k0) * 2 > pc.xb_bytes) return MK_ERR_PLAN;
+          int g = t.group;
+          if (g < 0 || g >= T.ngroups || t.row0 != g * 16 * T.gs) return MK_ERR_PLAN;
+          if (t.k0 != next_k[g] || t.k1 <= t.k0 || t.ks != next_piece[g]) return MK_ERR_PLAN;
+          if (t.k0 % kKBlock) return MK_ERR_PLAN;
+          next_k[g] = t.k1;
+          next_piece[g] += 1;
+          if (t.nchunks != t.nsub * ((t.k1 - t.k0 + kKBlock - 1) / kKBlock)) return MK_ERR_PLAN;
+          covered += (long long)std::min(16 * t.nsub, M - t.row0) * (t.k1 - t.k0);
         }
-      for (int v : seen)
-        if (v != 1) return MK_ERR_PLAN;
-      if (covered != (long long)stage_rows(pc, st) * stage_k(pc, st)) return MK_ERR_PLAN;
+      for (int g = 0; g < T.ngroups; ++g)
+        if (next_k[g] != K || next_piece[g] != group_pieces[st][g]) return MK_ERR_PLAN;
+      if (covered != (long long)M * K) return MK_ERR_PLAN;
     }
   }
   // (2) deadlock freedom: execute the in-order streams abstractly; a task may
@@ -254,7 +284,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
         while (pc_[c] < S[c].size()) {
           const Task& t = S[c][pc_[c]];
           if (t.wait_ctr >= 0 && given[t.wait_ctr] < total_signals[t.wait_ctr]) break;
-          if (t.signal_ctr >= 0) given[t.signal_ctr] += 1;
+          if (t.signal_ctr >= 0 && (t.flags & kTaskSignal)) given[t.signal_ctr] += 1;
           pc_[c] += 1;
           done += 1;
           progress = true;
