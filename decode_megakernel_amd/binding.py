@@ -60,6 +60,7 @@ class PlanStats(ctypes.Structure):
 EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
            "mk_reset", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
+STAT_WORDS = 64  # per-CU trace totals, see mk_copy_trace
 
 _lib = None
 
@@ -202,11 +203,11 @@ class DecodeEngine:
         if cap.value <= 0:
             return None
         n, c = n_cu.value, cap.value
-        buf = torch.empty(n * c * 4 + n * 32, dtype=torch.int64, device="cuda")
+        buf = torch.empty(n * c * 4 + n * STAT_WORDS, dtype=torch.int64, device="cuda")
         _check(lib().mk_copy_trace(self.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel() * 8,
                                    ctypes.byref(n_cu), ctypes.byref(cap), _stream_handle(None)), "mk_copy_trace")
         arr = buf.cpu().numpy().view("uint64")
-        return arr[: n * c * 4].reshape(n, c, 4), arr[n * c * 4:].reshape(n, 32)
+        return arr[: n * c * 4].reshape(n, c, 4), arr[n * c * 4:].reshape(n, STAT_WORDS)
 
     def status(self, stream=None) -> int:
         s = ctypes.c_uint32()

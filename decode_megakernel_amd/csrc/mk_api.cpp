@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -106,11 +107,12 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
   p.ncu = ncu;
   p.xb_bytes = xb;
   p.mfma_min_batch = mfma_min;
+  p.gemv_mode = env_int("MK_GEMV_MODE", 0);
   return p;
 }
 
 static int xb_for(int lds_max, int nslot) {
-  long long xb = (long long)lds_max - (long long)nslot * kChunkBytes - kRedBytes - 512;
+  long long xb = (long long)lds_max - (long long)nslot * kChunkBytes - kRedBytes - kCtrlBytes;
   xb &= ~255LL;
   return (int)xb;
 }
@@ -120,7 +122,7 @@ int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats*
   if (rc) return rc;
   if (!out || n_cu < 1 || batch < 1 || batch > cfg->max_batch) return MK_ERR_INVALID_ARG;
   const int nslot = env_int("MK_NSLOT", 7);
-  PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot), env_int("MK_MFMA_MIN_BATCH", 8));
+  PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot), std::min(8, std::max(1, env_int("MK_MFMA_MIN_BATCH", 8))));
   Plan P;
   rc = build_plan(pc, batch, &P);
   if (rc) return rc;
@@ -180,7 +182,8 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
     delete h;
     return MK_ERR_UNSUPPORTED;
   }
-  h->mfma_min_batch = env_int("MK_MFMA_MIN_BATCH", 8);
+  // the VALU path handles up to 7 sequences; larger batches use MFMA tiles
+  h->mfma_min_batch = std::min(8, std::max(1, env_int("MK_MFMA_MIN_BATCH", 8)));
   h->timeout_ticks = (uint64_t)env_int("MK_SPIN_TIMEOUT_MS", 2000) * 100000ull;
 
   const int d = cfg->hidden, bc = cfg->max_batch, hd = cfg->head_dim, nkv = cfg->n_kv_heads;
@@ -280,7 +283,7 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   }
   h->trace_cap = env_int("MK_TRACE", 0);
   if (h->trace_cap > 0) {
-    size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * 32) * 8;
+    size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * kStatWords) * 8;
     if (hipMalloc(&h->trace, tb) != hipSuccess || hipMemset(h->trace, 0, tb) != hipSuccess) {
       (void)hipFree(h->d_layers);
       (void)hipFree(h->ws);
@@ -452,7 +455,7 @@ int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t
   *n_cu = h->ncu;
   *cap = h->trace_cap;
   if (!h->trace || !dst) return MK_OK;
-  const size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * 32) * 8;
+  const size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * kStatWords) * 8;
   if (bytes < (int64_t)tb) return MK_ERR_INVALID_ARG;
   if (hipMemcpyAsync(dst, h->trace, tb, hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   return MK_OK;

@@ -31,6 +31,8 @@ constexpr int kGroupSub = 4;                 // 16-row sub-tiles per row group (
 // floats), whichever is larger for group <= 4 at head_dim 128 and group <= 8
 // at head_dim 64.
 constexpr int kRedBytes = 2 * 4 * 8 * (64 + 4) * 4;
+constexpr int kStatWords = 64;               // trace: per-CU phase totals (uint64 words)
+constexpr int kCtrlBytes = 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
 constexpr int kApartGroup = 8;               // group slots per attention partial
 
 enum Stage : int32_t { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_LM = 5, ST_EMBED = 6 };
@@ -42,7 +44,7 @@ struct Task {
   int32_t stage;
   int32_t layer;
   int32_t row0;        // GEMV: first logical output row; EMBED: first column
-  int32_t nsub;        // GEMV: 16-row sub-tiles of the group (1..4); EMBED: number of columns
+  int32_t nsub;        // GEMV: 16-row sub-tiles of the task (1..4*tiles_per_wave); EMBED: number of columns
   int32_t k0, k1;      // GEMV: K range, k0 a multiple of 512
   int32_t ks, nks;     // GEMV: this task's piece index among the nks pieces that split the group's K
   int32_t group;       // GEMV: row group (counter index within the stage when nks > 1)
@@ -54,6 +56,15 @@ struct Task {
   int32_t pad;
 };
 static_assert(sizeof(Task) == 64, "Task must be 64 bytes");
+
+// 16-row sub-tiles one compute wave accumulates at once in a GEMV task
+// (registers: tiles x 16 rows x batch for the VALU path, 4 per tile for
+// MFMA).  A task holds up to 4x this many sub-tiles; wave w owns sub-tiles
+// w, w+4, ...
+MK_HD constexpr int tiles_per_wave(int nb_valu) {
+  return nb_valu <= 0 ? 8 : nb_valu <= 2 ? 2 : 1;
+}
+constexpr int kMaxTilesPerWave = 8;
 
 // Counter indices: EMBED, then 5 per layer, then LM.
 MK_HD inline int ctr_embed() { return 0; }
@@ -144,6 +155,7 @@ struct PlanCfg {
   int ncu;
   int xb_bytes;         // LDS bytes available to stage a GEMV input slice
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
+  int gemv_mode = 0;    // 0: cheaper of row-owner / stream-K per stage, 1: row-owner, 2: stream-K
 };
 constexpr int kTaskSignal = 1;
 
@@ -159,6 +171,7 @@ struct Plan {
   int stage_tasks[6] = {0, 0, 0, 0, 0, 0};
   int stage_ksplit[6] = {0, 0, 0, 0, 0, 0};
   int stage_rows[6] = {0, 0, 0, 0, 0, 0};
+  int stage_owner[6] = {0, 0, 0, 0, 0, 0};  // 1: whole sub-tiles per CU over full K (no split)
   long long weight_bytes = 0;
   long long max_cu_weight_bytes = 0;
   double balance_min = 1.0;

@@ -28,6 +28,7 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 constexpr unsigned kCpSc1 = 16;  // cache policy: device scope (coherent across XCDs)
+constexpr unsigned kCpNt = 2;    // cache policy: non-temporal (streamed once)
 
 // Kernel arguments are read in place from the kernarg segment through a
 // constant-address-space pointer; `uni` re-establishes at a function's entry
@@ -47,11 +48,26 @@ __device__ __forceinline__ const MK_AS4 T* as_const(const T* p) {
 typedef const MK_AS4 Task* TaskP;
 // copy a 64-byte task descriptor out of constant memory (scalar loads)
 __device__ __forceinline__ Task load_task(TaskP p) {
+  // field by field (no type punning), so the copy stays in scalar registers
+#define MK_TF(f) t.f = __builtin_amdgcn_readfirstlane(p->f)
   Task t;
-  const MK_AS4 int32_t* src = (const MK_AS4 int32_t*)p;
-  int32_t* dst = (int32_t*)&t;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(Task) / 4); ++i) dst[i] = src[i];
+  MK_TF(type);
+  MK_TF(stage);
+  MK_TF(layer);
+  MK_TF(row0);
+  MK_TF(nsub);
+  MK_TF(k0);
+  MK_TF(k1);
+  MK_TF(ks);
+  MK_TF(nks);
+  MK_TF(group);
+  MK_TF(part_slot);
+  MK_TF(wait_ctr);
+  MK_TF(signal_ctr);
+  MK_TF(nchunks);
+  MK_TF(flags);
+  t.pad = 0;
+#undef MK_TF
   return t;
 }
 __device__ __forceinline__ TaskP uni(TaskP p) {
@@ -122,18 +138,44 @@ __device__ __forceinline__ u32x4 lds_ld16(const char* p) { return *(const u32x4*
 __device__ __forceinline__ void lds_st16(char* p, u32x4 v) { *(u32x4*)p = v; }
 
 // ------------------------------------------------------------ CU control
+struct CState {
+  uint64_t t_stream;  // trace: when the task's last chunk was consumed
+  uint64_t w_empty;   // trace: ticks spent waiting for the loader
+  uint64_t w_bar;     // trace: ticks spent in compute barriers
+  uint64_t t_math;    // trace: ticks spent on chunk math
+  uint64_t t_stage;   // trace: ticks spent staging GEMV inputs
+  uint64_t t_epi;     // trace: ticks spent in reductions and epilogues
+  int gen;      // compute-barrier generation
+  int q;        // chunk sequence number of the current task's first chunk
+  int last_dep; // counter of the last dependency already satisfied
+  int x_stage, x_layer, x_k0, x_k1;  // signature of the staged input slice
+  int r_stage, r_layer;              // stage whose RMS scales are in Ctrl::rms
+};
+
 struct Ctrl {
+  CState cs[kComputeWaves];  // per compute wave
   int ready[kMaxSlots];
   int freed[kMaxSlots];
   int dep;
   int bar;
   int fin;
   int abort;
+  unsigned long long lmkey[kMaxBatch];  // this CU's best LM-head key per sequence
   int pos[kMaxBatch];
   int slen[kMaxBatch];
   int tok[kMaxBatch];
   float rms[kMaxBatch];
 };
+
+static_assert(sizeof(Ctrl) <= kCtrlBytes, "control block exceeds its LDS budget");
+
+// Dynamic LDS of the step kernel: weight/KV ring, staged GEMV input,
+// reduction scratch, control block.  Every role derives its pointers from
+// this array so that LDS accesses compile to ds_* instructions.
+extern __shared__ __attribute__((aligned(16))) char mk_lds[];
+__device__ __forceinline__ char* xb_stage(DArgs A) { return mk_lds + (size_t)A->nslot * kChunkBytes; }
+__device__ __forceinline__ float* red_scratch(DArgs A) { return (float*)(xb_stage(A) + A->xb_bytes); }
+__device__ __forceinline__ Ctrl* ctrl_block(DArgs A) { return (Ctrl*)((char*)red_scratch(A) + kRedBytes); }
 
 __device__ __forceinline__ int lds_ld_acq(int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
 __device__ __forceinline__ void lds_st_rel(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
@@ -197,7 +239,7 @@ __device__ __forceinline__ unsigned long long* keys_ptr(DArgs A) {
 
 // Wait (one wave, all 64 lanes) until every shard of counter `ctr` reached
 // the count the schedule expects.
-__device__ bool wait_counter(DArgs A, Ctrl* c, int ctr, int lane) {
+__device__ __forceinline__ bool wait_counter(DArgs A, Ctrl* c, int ctr, int lane) {
   A = uni(A);
   const uint32_t* p = bank_ptr(A, A->bank) + lane * A->ctr_stride + ctr;
   const int e = as_const(A->expect)[ctr * kShards + lane];
@@ -428,7 +470,7 @@ __device__ __forceinline__ RowBase sub_rows(DArgs A, const Task& t, int sub) {
   const int r = t.row0 + 16 * sub;
   RowBase rb;
   rb.nrows = min(16, stage_M(A, t.stage) - r);
-  const MK_AS4 LayerW* w = as_const(A->layers) + (t.stage == ST_LM ? 0 : t.layer);
+  const MK_AS4 LayerW* w = as_const(A->layers) + __builtin_amdgcn_readfirstlane(t.stage == ST_LM ? 0 : t.layer);
   switch (t.stage) {
     case ST_QKV: {
       const uint16_t *q = w->q, *k = w->k, *v = w->v;
@@ -561,15 +603,17 @@ __device__ __forceinline__ void ring_issued(DArgs A, Ctrl* c, LoaderRing& R, int
   while (R.slot >= A->nslot) R.slot -= A->nslot;
 }
 
-__device__ void loader_main(DArgs A, char* ring, Ctrl* c, int cu, int lw, int lane) {
+__device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
   A = uni(A);
+  char* ring = mk_lds;
+  Ctrl* c = ctrl_block(A);
   const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
   const int nt = as_const(A->task_off)[cu + 1] - as_const(A->task_off)[cu];
   const int rpc = 4096 / A->hd;
   // per-sequence lengths into registers before any load is in flight
   SeqLens sl;
 #pragma unroll
-  for (int i = 0; i < kMaxBatch; ++i) sl.v[i] = i < A->b ? c->slen[i] : 1;
+  for (int i = 0; i < kMaxBatch; ++i) sl.v[i] = __builtin_amdgcn_readfirstlane(i < A->b ? c->slen[i] : 1);
   const uint64_t t_start = A->trace ? now_ticks() : 0;
   LoaderRing R{lw, lw % A->nslot, -1, 0, 0};
   int qbase = 0;
@@ -623,15 +667,16 @@ __device__ void loader_main(DArgs A, char* ring, Ctrl* c, int cu, int lw, int la
     if (lane == 0) lds_flag_write(&c->ready[R.prev_slot], R.prev_q + 1);
   }
   if (A->trace && lane == 0) {
-    uint64_t* st = A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * 32;
+    uint64_t* st = A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords;
     st[lw] = R.wfull;
     if (lw == 0) st[13] = now_ticks() - t_start;
   }
 }
 
 // ================================================================ compute
-__device__ int attn_task_chunks(DArgs A, const Ctrl* c, int cu, int rpc) {
+__device__ __forceinline__ int attn_task_chunks(DArgs A, int cu, int rpc) {
   A = uni(A);
+  const Ctrl* c = ctrl_block(A);
   long long W = attn_total(c, A->b, A->nkv);
   long long pos = cu_lo(cu, W, A->ncu), hi = cu_lo(cu + 1, W, A->ncu);
   Piece P;
@@ -639,19 +684,6 @@ __device__ int attn_task_chunks(DArgs A, const Ctrl* c, int cu, int rpc) {
   while (next_piece(c, A->b, A->nkv, rpc, pos, hi, P)) n += P.nch;
   return n;
 }
-struct CState {
-  uint64_t t_stream;  // trace: when the task's last chunk was consumed
-  uint64_t w_empty;   // trace: ticks spent waiting for the loader
-  uint64_t w_bar;     // trace: ticks spent in compute barriers
-  uint64_t t_math;    // trace: ticks spent on chunk math
-  uint64_t t_stage;   // trace: ticks spent staging GEMV inputs
-  uint64_t t_epi;     // trace: ticks spent in reductions and epilogues
-  int gen;      // compute-barrier generation
-  int q;        // chunk sequence number of the current task's first chunk
-  int last_dep; // counter of the last dependency already satisfied
-  int x_stage, x_layer, x_k0, x_k1;  // signature of the staged input slice
-  int r_stage, r_layer;              // stage whose RMS scales are in Ctrl::rms
-};
 
 __device__ __forceinline__ bool wait_chunk(DArgs A, Ctrl* c, int gq, uint64_t& wait_ticks) {
   const int slot = gq % A->nslot;
@@ -667,13 +699,34 @@ __device__ __forceinline__ void free_chunk(DArgs A, Ctrl* c, int gq, int lane) {
 }
 
 // Wave-wide sum over 16-lane groups (lanes l, l^1, ..., l^8).
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+// DPP lane moves within 16-lane rows: quad_perm [1,0,3,2] (lane ^ 1),
+// quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (lane i of each 8 <- 7-i),
+// row_mirror (lane i of each 16 <- 15-i), row_ror:8 (lane ^ 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppRor8 = 0x128;
+// Sum over aligned groups of N lanes (N = 2, 4, 8 or 16); every lane of a
+// group gets the group's total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2..16 lanes");
+  v += dpp_f<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppMirror>(v);
   return v;
 }
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float sum16(float v) { return group_sum<16>(v); }
 
 // Order-preserving 64-bit key: larger logit first, then lower index.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
@@ -848,44 +901,59 @@ __device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, i
                                (uint32_t)__shfl_xor((int)(uint32_t)key, m);
         key = o > key ? o : key;
       }
-      if (row == 0 && n < A->b && key) __hip_atomic_fetch_max(keys_ptr(A) + n, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (row == 0 && n < A->b && key) __hip_atomic_fetch_max(&c->lmkey[n], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       break;
     }
   }
 }
 
-// One GEMV task: a row group of nsub 16-row sub-tiles over K range [k0, k1).
-// Compute wave w owns sub-tile w: it consumes that sub-tile's chunks, reduces
-// across its own lanes and runs the epilogue, with no cross-wave reduction.
-// A group whose K range is split over several tasks publishes partials; the
+// One GEMV task: nsub 16-row sub-tiles over K range [k0, k1).  Compute wave
+// w owns sub-tiles w, w+4, ... (at most tiles_per_wave(NB) of them): it
+// consumes their chunks, reduces each across its own lanes and runs the
+// epilogue, with no cross-wave reduction.  A sub-tile whose K range is split
+// over several tasks (nks > 1, one sub-tile per wave) publishes partials; the
 // last piece to finish sums them in piece order and runs the epilogue.
+// NB > 0: VALU dot products for NB sequences; NB == 0: MFMA (batch <= 16).
 template <int NB>
-__device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, Ctrl* c, CState& s, int cu,
-                          int w, int lane) {
+__device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lane) {
+  constexpr int TPW = tiles_per_wave(NB);
+  constexpr int NV = NB > 0 ? NB : 1;
+  constexpr int kResidTiles = 2;  // owned sub-tiles whose residual is prefetched
   A = uni(A);
+  char* ring = mk_lds;
+  char* xb = xb_stage(A);
+  float* red = red_scratch(A);
+  Ctrl* c = ctrl_block(A);
+  CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
   const int nsub = t.nsub;
-  const bool own = w < nsub;
+  const int nown = nsub > w ? min(TPW, (nsub - w + kComputeWaves - 1) / kComputeWaves) : 0;
   const int M = stage_M(A, t.stage);
-  const int kb0 = t.k0 / kKBlock, nkb = (t.k1 - t.k0 + kKBlock - 1) / kKBlock;
-  const int lr0 = t.row0 + 16 * w;  // first row of the owned sub-tile
+  const int nkb = (t.k1 - t.k0 + kKBlock - 1) / kKBlock;
   const int row = lane & 15;
-  // residual of the owned rows, prefetched while the weights stream
-  float resid[4] = {0.f, 0.f, 0.f, 0.f};
-  if (own && (t.stage == ST_O || t.stage == ST_DOWN)) {
-    const float* hin = t.stage == ST_DOWN ? A->hmid + (size_t)t.layer * A->bcap * A->d : A->hres + (size_t)t.layer * A->bcap * A->d;
+  const bool has_resid = t.stage == ST_O || t.stage == ST_DOWN;
+  const float* hin = t.stage == ST_DOWN ? A->hmid + (size_t)t.layer * A->bcap * A->d
+                                        : A->hres + (size_t)t.layer * A->bcap * A->d;
+  // residuals of the first owned rows, prefetched while the weights stream
+  float resid[kResidTiles][4];
+#pragma unroll
+  for (int i = 0; i < kResidTiles; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = (lane >> 4) + 4 * j;
-      if (n < A->b && lr0 + row < M) resid[j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4));
+      resid[i][j] = 0.f;
+      const int n = (lane >> 4) + 4 * j, lr = t.row0 + 16 * (w + kComputeWaves * i) + row;
+      if (has_resid && i < nown && n < A->b && lr < M) resid[i][j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4));
     }
+  float vacc[TPW][16][NV];
+  f32x4 macc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    macc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int n = 0; n < NV; ++n) vacc[i][j][n] = 0.f;
   }
-  float vacc[16][NB];
-  f32x4 macc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-#pragma unroll
-    for (int n = 0; n < NB; ++n) vacc[j][n] = 0.f;
   // K windows that fit the LDS staging buffer
   int wkb = ((A->xb_bytes / (2 * A->b)) - 8) / kKBlock;
   if (wkb < 1) wkb = 1;
@@ -896,28 +964,30 @@ __device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, C
     if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane)) return false;
     if (A->trace) s.t_stage += now_ticks() - ts0;
     const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0;
-    if (own) {
-      for (int kb = wb; kb < we; ++kb) {
-        const int gq = s.q + kb * nsub + w;
+    for (int kb = wb; kb < we && nown > 0; ++kb) {
+      const int kl = (kb - wb) * kKBlock;
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        if (i >= nown) break;
+        const int gq = s.q + kb * nsub + w + kComputeWaves * i;
         if (!wait_chunk(A, c, gq, s.w_empty)) return false;
         const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
-        const int kl = (kb - wb) * kKBlock;
         const uint64_t tm0 = A->trace ? now_ticks() : 0;
-        if (!A->mfma) valu_chunk<NB>(slot, xb, ksp, kl + 8 * lane, klen, lane, vacc);
-        else mfma_chunk(slot, xb, ksp, kl, klen, A->b, lane, macc);
+        if constexpr (NB > 0) valu_chunk<NB>(slot, xb, ksp, kl + 8 * lane, klen, lane, vacc[i]);
+        else mfma_chunk(slot, xb, ksp, kl, klen, A->b, lane, macc[i]);
         free_chunk(A, c, gq, lane);
         if (A->trace) s.t_math += now_ticks() - tm0;
       }
     }
   }
-  (void)kb0;
   const uint64_t te0 = A->trace ? now_ticks() : 0;
-  // owned sub-tile totals -> this wave's LDS scratch as [16 rows][16 n]
+  // owned sub-tile i's totals -> this wave's LDS scratch as [16 rows][16 n],
+  // read back with lanes mapped to (row = lane & 15, n = lane / 16 + 4 j)
   float* rw = red + w * 1024;
-  if (own) {
-    if (!A->mfma) {
+  auto tile_values = [&](int i, float (&val)[4], float (&up)[4]) {
+    if constexpr (NB > 0) {
       float tot[NB];
-      valu_reduce<NB>(vacc, lane, tot);
+      valu_reduce<NB>(vacc[i], lane, tot);
       if ((lane & 3) == 0) {
         const int rr = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
 #pragma unroll
@@ -925,18 +995,20 @@ __device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, C
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rw[(4 * (lane >> 4) + i) * 16 + (lane & 15)] = macc[i];
+      for (int q = 0; q < 4; ++q) rw[(4 * (lane >> 4) + q) * 16 + (lane & 15)] = macc[i][q];
     }
-  }
-  float val[4], up[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = (lane >> 4) + 4 * j;
-    val[j] = own ? rw[row * 16 + n] : 0.f;
-    up[j] = (own && t.stage == ST_GU && row < 8) ? rw[(row + 8) * 16 + n] : 0.f;
-  }
-  bool do_epi = own;
+    for (int j = 0; j < 4; ++j) {
+      const int n = (lane >> 4) + 4 * j;
+      val[j] = rw[row * 16 + n];
+      up[j] = (t.stage == ST_GU && row < 8) ? rw[(row + 8) * 16 + n] : 0.f;
+    }
+  };
   if (t.nks > 1) {
+    // split K: one sub-tile per wave (nsub <= 4)
+    const bool own = nown > 0;
+    float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+    if (own) tile_values(0, val, up);
     float* pb = A->part + (size_t)(t.part_slot + t.ks) * 1024 + w * 256;
     if (own) {
 #pragma unroll
@@ -953,8 +1025,7 @@ __device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, C
     }
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     const bool fin = lds_ld_acq(&c->fin) != 0;
-    do_epi = own && fin;
-    if (do_epi) {
+    if (own && fin) {
       const float* p0 = A->part + (size_t)t.part_slot * 1024 + w * 256;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -967,16 +1038,43 @@ __device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, C
         val[j] = v;
         up[j] = u;
       }
-    }
-  }
-  if (do_epi) {
+      const int lr0 = t.row0 + 16 * w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[j], lane);
+      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], lane);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (i >= nown) break;
+      float val[4], up[4];
+      tile_values(i, val, up);
+      const int lr0 = t.row0 + 16 * (w + kComputeWaves * i);
+      float rs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i < kResidTiles) {
+          rs[j] = resid[i < kResidTiles ? i : 0][j];
+        } else {
+          const int n = (lane >> 4) + 4 * j;
+          rs[j] = (has_resid && n < A->b && lr0 + row < M) ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4)) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], lane);
+    }
   }
   if (t.flags & kTaskSignal) {
     wait_mem();
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
-    if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
+    if (w == 0) {
+      if (t.stage == ST_LM && lane < A->b) {
+        // fold this CU's argmax keys into the global ones
+        const unsigned long long key = c->lmkey[lane];
+        if (key) __hip_atomic_fetch_max(keys_ptr(A) + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_mem();
+      }
+      if (lane == 0) signal_counter(A, t.signal_ctr, cu);
+    }
   }
   if (A->trace) s.t_epi += now_ticks() - te0;
   return true;
@@ -984,8 +1082,10 @@ __device__ bool gemv_task(DArgs A, TaskP tp, char* ring, char* xb, float* red, C
 
 // ---- embedding gather: h0 = E[token] for 64 columns, plus the first
 //      RMSNorm's input and per-16-column sums of squares.
-__device__ bool embed_task(DArgs A, TaskP tp, Ctrl* c, CState& s, int cu, int w, int lane) {
+__device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
+  Ctrl* c = ctrl_block(A);
+  CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
   const int tid = w * 64 + lane, n = tid >> 4, col = t.row0 + 4 * (tid & 15);
   float h[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1051,8 +1151,12 @@ __device__ __forceinline__ void rope_head(DArgs A, const float* src /* head base
 }
 
 template <int HD, int GM>
-__device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
+__device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
+  char* ring = mk_lds;
+  float* red = red_scratch(A);
+  Ctrl* c = ctrl_block(A);
+  CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
   constexpr int LPR = HD / 8, RP = 64 / LPR, RPC = 4096 / HD;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -1064,8 +1168,21 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
   int qc = s.q, pidx = 0;
   const MK_AS4 LayerW& lw = as_const(A->layers)[l];
   const int stride_st = kComputeWaves * GM * (HD + 4);
+  // trace: attention phase totals of compute wave 0 (per-CU stats words 32..40)
+  uint64_t* ast = (A->trace && w == 0 && lane == 0)
+                      ? A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32
+                      : nullptr;
+  uint64_t tlast = ast ? now_ticks() : 0;
+  auto mark = [&](int k) {
+    if (ast) {
+      const uint64_t tn = now_ticks();
+      ast[k] += tn - tlast;
+      tlast = tn;
+    }
+  };
   while (next_piece(c, A->b, A->nkv, RPC, pos, hi, P)) {
     const int p = c->slen[P.i] - 1;
+    if (ast) ast[7] += 1;
     const float* qrow = A->qkv + ((size_t)l * A->bcap + P.i) * A->nqkv;
     float q[GM][8], o[GM][8];
     SoftState st[GM];
@@ -1084,37 +1201,67 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
         for (int u = 0; u < 8; ++u) q[h][u] = 0.f;
       }
     }
+    mark(0);
     // cached rows, streamed by the loader
     for (int ch = 0; ch < P.nch; ++ch) {
       const int gq = qc + ch;
       if ((gq & (kComputeWaves - 1)) != w) continue;
+      const uint64_t tw0 = ast ? now_ticks() : 0;
       if (!wait_chunk(A, c, gq, s.w_empty)) return false;
+      if (ast) ast[9] += now_ticks() - tw0;
       const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
       const int rows = min(RPC, P.ncached - ch * RPC);
-#pragma unroll 2
-      for (int pass = 0; pass < RPC / RP; ++pass) {
+      // scores of every row of the chunk first (lane group gi holds rows
+      // gi, gi + RP, ...), then one online-softmax rescale per chunk
+      constexpr int NP = RPC / RP;  // passes per chunk
+      float sc[GM][NP];
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
         const int row = pass * RP + gi;
-        u32x4 kv = lds_ld16(slot + row * HD * 2 + e0 * 2);
-        u32x4 vv = lds_ld16(slot + 8192 + row * HD * 2 + e0 * 2);
-        float kf[8], vf[8];
-        unpack8(kv, kf);
-        unpack8(vv, vf);
+        float kf[8];
+        unpack8(lds_ld16(slot + row * HD * 2 + e0 * 2), kf);
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          float d = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) d += q[h][u] * kf[u];
+          sc[h][pass] = d;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h >= G) continue;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+          const float v = group_sum<LPR>(sc[h][pass]);
+          sc[h][pass] = pass * RP + gi < rows ? v : -INFINITY;
+          mx = fmaxf(mx, sc[h][pass]);
+        }
+        const float mn = fmaxf(st[h].m, mx);
+        const float fa = mn == -INFINITY ? 1.f : exp2f(st[h].m - mn);
+        float lsum = 0.f;
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+          const float pw = sc[h][pass] == -INFINITY ? 0.f : exp2f(sc[h][pass] - mn);
+          sc[h][pass] = pw;
+          lsum += pw;
+        }
+        st[h].l = st[h].l * fa + lsum;
+        st[h].m = mn;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[h][u] *= fa;
+      }
+#pragma unroll
+      for (int pass = 0; pass < NP; ++pass) {
+        const int row = pass * RP + gi;
+        float vf[8];
+        unpack8(lds_ld16(slot + 8192 + row * HD * 2 + e0 * 2), vf);
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
           if (h >= G) continue;
-          float sc = 0.f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) sc += q[h][u] * kf[u];
-#pragma unroll
-          for (int m = 1; m < LPR; m <<= 1) sc += __shfl_xor(sc, m);
-          if (row < rows) {
-            const float mn = fmaxf(st[h].m, sc);
-            const float fa = exp2f(st[h].m - mn), pw = exp2f(sc - mn);
-            st[h].l = st[h].l * fa + pw;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) o[h][u] = o[h][u] * fa + pw * vf[u];
-            st[h].m = mn;
-          }
+          for (int u = 0; u < 8; ++u) o[h][u] += sc[h][pass] * vf[u];
         }
       }
       free_chunk(A, c, gq, lane);
@@ -1144,8 +1291,7 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
         float sc = 0.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) sc += q[h][u] * kn[u];
-#pragma unroll
-        for (int m = 1; m < LPR; m <<= 1) sc += __shfl_xor(sc, m);
+        sc = group_sum<LPR>(sc);
         if (gi == 0) {
           const float mn = fmaxf(st[h].m, sc);
           const float fa = exp2f(st[h].m - mn), pw = exp2f(sc - mn);
@@ -1156,6 +1302,7 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
         }
       }
     }
+    mark(1);
     // merge the lane groups of this wave
 #pragma unroll
     for (int msk = LPR; msk < 64; msk <<= 1) {
@@ -1187,6 +1334,14 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
       }
     }
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    mark(2);
+    const int s_i = c->slen[P.i];
+    const int c_first = cu_of(P.seg_start, W, A->ncu), c_last = cu_of(P.seg_start + s_i - 1, W, A->ncu);
+    // CUs whose range is empty (fewer rows than CUs) hold no piece
+    const int npieces = W >= A->ncu ? c_last - c_first + 1
+                                   : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
+    const int pstride = GM * (HD + 4);
+    uint16_t* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
     if (w == 0) {
       // merge the 4 wave states (lane group 0 holds 8 elements per lane)
       const float* s0 = red + (pidx & 1) * stride_st;
@@ -1210,14 +1365,21 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
           M[h] = mn;
         }
       }
-      const int s_i = c->slen[P.i];
-      const int c_first = cu_of(P.seg_start, W, A->ncu), c_last = cu_of(P.seg_start + s_i - 1, W, A->ncu);
-      // CUs whose range is empty (fewer rows than CUs) hold no piece
-      const int npieces = W >= A->ncu ? c_last - c_first + 1
-                                     : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
-      bool finisher = npieces == 1;
-      const int pstride = GM * (HD + 4);
-      if (!finisher) {
+      int fin = 0;
+      if (npieces == 1) {
+        // the whole segment is here: normalise and store
+        if (gi == 0) {
+#pragma unroll
+          for (int h = 0; h < GM; ++h) {
+            if (h >= G) continue;
+            const float inv = 1.0f / Lsum[h];
+            co_store16(ob, (uint32_t)((h * HD + e0) * 2),
+                       u32x4{pack_bf2(O[h][0] * inv, O[h][1] * inv), pack_bf2(O[h][2] * inv, O[h][3] * inv),
+                             pack_bf2(O[h][4] * inv, O[h][5] * inv), pack_bf2(O[h][6] * inv, O[h][7] * inv)});
+          }
+        }
+      } else {
+        // publish this piece; the last piece of the segment to arrive merges
         float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
         if (gi == 0) {
 #pragma unroll
@@ -1234,120 +1396,116 @@ __device__ bool attn_task(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CS
         uint32_t old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(A->seg_ctr + P.sid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
-        finisher = (int)old == npieces - 1;
-        if (finisher) {
-          if (lane == 0) __hip_atomic_store(A->seg_ctr + P.sid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          // merge every piece of the segment, in piece order: (1) the
-          // per-head maximum over pieces, one piece per lane; (2) the
-          // weighted sums, one piece per lane group, then across groups.
-          auto piece_cu = [&](int pc) -> int {
-            return W >= A->ncu ? c_first + pc : cu_of(P.seg_start + pc, W, A->ncu);
-          };
-#pragma unroll
-          for (int h = 0; h < GM; ++h) M[h] = -INFINITY;
+        fin = (int)old == npieces - 1;
+        if (fin && lane == 0) __hip_atomic_store(A->seg_ctr + P.sid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) lds_st_rel(&c->fin, fin);
+      mark(3);
+    }
+    if (npieces > 1) {
+      if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+      if (lds_ld_acq(&c->fin)) {
+        // merge every piece of the segment: compute wave w takes heads
+        // w, w + 4; LPP lanes cover one piece's head vector, 64 / LPP pieces
+        // per pass, all loads of kMergeUnroll passes issued together
+        constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeUnroll = 8;
+        const int sub = lane / LPP, el = (lane % LPP) * 4;
+        auto piece_src = [&](int pc) -> const float* {
+          const int pcu = W >= A->ncu ? c_first + pc : cu_of(P.seg_start + pc, W, A->ncu);
+          return A->apart + (size_t)(pcu + P.sid) * pstride;
+        };
+        for (int h = w; h < G; h += kComputeWaves) {
+          // maximum over the pieces' running maxima
+          float mv = -INFINITY;
           for (int p0 = 0; p0 < npieces; p0 += 64) {
             const int pc = p0 + lane;
-            const float* src = A->apart + (size_t)(piece_cu(pc < npieces ? pc : 0) + P.sid) * pstride;
+            if (pc < npieces) mv = fmaxf(mv, co_loadf(piece_src(pc), (uint32_t)((h * (HD + 4) + HD) * 4)));
+          }
+          mv = group_max<16>(mv);
+          mv = fmaxf(mv, __shfl_xor(mv, 16));
+          mv = fmaxf(mv, __shfl_xor(mv, 32));
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          float lsum = 0.f;
+          for (int p0 = 0; p0 < npieces; p0 += PPI * kMergeUnroll) {
+            u32x4 ov[kMergeUnroll];
+            float m2[kMergeUnroll], l2[kMergeUnroll];
 #pragma unroll
-            for (int h = 0; h < GM; ++h) {
-              if (h >= G) continue;
-              float mv = pc < npieces ? co_loadf(src, (uint32_t)((h * (HD + 4) + HD) * 4)) : -INFINITY;
+            for (int k = 0; k < kMergeUnroll; ++k) {
+              const int pc = p0 + k * PPI + sub;
+              const float* src = piece_src(pc < npieces ? pc : 0);
+              ov[k] = co_load16(src, (uint32_t)((h * (HD + 4) + el) * 4));
+              m2[k] = co_loadf(src, (uint32_t)((h * (HD + 4) + HD) * 4));
+              l2[k] = co_loadf(src, (uint32_t)((h * (HD + 4) + HD + 1) * 4));
+            }
 #pragma unroll
-              for (int m = 32; m >= 1; m >>= 1) mv = fmaxf(mv, __shfl_xor(mv, m));
-              M[h] = fmaxf(M[h], mv);
+            for (int k = 0; k < kMergeUnroll; ++k) {
+              const int pc = p0 + k * PPI + sub;
+              const float f = (pc < npieces && m2[k] != -INFINITY) ? exp2f(m2[k] - mv) : 0.f;
+              acc[0] += f * __uint_as_float(ov[k].x);
+              acc[1] += f * __uint_as_float(ov[k].y);
+              acc[2] += f * __uint_as_float(ov[k].z);
+              acc[3] += f * __uint_as_float(ov[k].w);
+              lsum += f * l2[k];
             }
           }
 #pragma unroll
-          for (int h = 0; h < GM; ++h) {
-            Lsum[h] = 0.f;
+          for (int msk = LPP; msk < 64; msk <<= 1) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) O[h][u] = 0.f;
+            for (int u = 0; u < 4; ++u) acc[u] += __shfl_xor(acc[u], msk);
+            lsum += __shfl_xor(lsum, msk);
           }
-          constexpr int PPW = 64 / LPR;  // pieces per pass
-#pragma unroll 2
-          for (int p0 = 0; p0 < npieces; p0 += PPW) {
-            const int pc = p0 + gi;
-            if (pc < npieces) {
-              const float* src = A->apart + (size_t)(piece_cu(pc) + P.sid) * pstride;
-#pragma unroll
-              for (int h = 0; h < GM; ++h) {
-                if (h >= G) continue;
-                u32x4 a0 = co_load16(src, (uint32_t)((h * (HD + 4) + e0) * 4));
-                u32x4 a1 = co_load16(src, (uint32_t)((h * (HD + 4) + e0 + 4) * 4));
-                const float m2 = co_loadf(src, (uint32_t)((h * (HD + 4) + HD) * 4));
-                const float l2 = co_loadf(src, (uint32_t)((h * (HD + 4) + HD + 1) * 4));
-                const float f = M[h] == -INFINITY ? 0.f : exp2f(m2 - M[h]);
-                float ov[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
-                               __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
-#pragma unroll
-                for (int u = 0; u < 8; ++u) O[h][u] += f * ov[u];
-                Lsum[h] += f * l2;
-              }
-            }
-          }
-#pragma unroll
-          for (int msk = LPR; msk < 64; msk <<= 1) {
-#pragma unroll
-            for (int h = 0; h < GM; ++h) {
-              if (h >= G) continue;
-#pragma unroll
-              for (int u = 0; u < 8; ++u) O[h][u] += __shfl_xor(O[h][u], msk);
-              Lsum[h] += __shfl_xor(Lsum[h], msk);
-            }
+          if (sub == 0) {
+            const float inv = 1.0f / lsum;
+            co_store8(ob, (uint32_t)((h * HD + el) * 2),
+                      u32x2{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)});
           }
         }
-      }
-      if (finisher && gi == 0) {
-        uint16_t* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim;
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          if (h >= G) continue;
-          const float inv = 1.0f / Lsum[h];
-          co_store16(ob, (uint32_t)((((size_t)(P.g * G + h)) * HD + e0) * 2),
-                     u32x4{pack_bf2(O[h][0] * inv, O[h][1] * inv), pack_bf2(O[h][2] * inv, O[h][3] * inv),
-                           pack_bf2(O[h][4] * inv, O[h][5] * inv), pack_bf2(O[h][6] * inv, O[h][7] * inv)});
-        }
+        mark(4);
+        if (ast) ast[8] += 1;
       }
     }
+    mark(5);
     qc += P.nch;
     ++pidx;
   }
   wait_mem();
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
+  mark(6);
   return true;
 }
 
 template <int HD>
-__device__ bool attn_dispatch(DArgs A, TaskP tp, char* ring, float* red, Ctrl* c, CState& s, int cu, int w, int lane) {
+__device__ __forceinline__ bool attn_dispatch(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
-  if (A->G <= 1) return attn_task<HD, 1>(A, tp, ring, red, c, s, cu, w, lane);
-  if (A->G <= 2) return attn_task<HD, 2>(A, tp, ring, red, c, s, cu, w, lane);
-  if (A->G <= 4) return attn_task<HD, 4>(A, tp, ring, red, c, s, cu, w, lane);
-  if constexpr (HD == 64) return attn_task<HD, 8>(A, tp, ring, red, c, s, cu, w, lane);
+  if (A->G <= 1) return attn_task<HD, 1>(A, tp, cu, w, lane);
+  if (A->G <= 2) return attn_task<HD, 2>(A, tp, cu, w, lane);
+  if (A->G <= 4) return attn_task<HD, 4>(A, tp, cu, w, lane);
+  if constexpr (HD == 64) return attn_task<HD, 8>(A, tp, cu, w, lane);
   return false;  // group > 4 at head_dim 128 is rejected at mk_create
 }
 
-__device__ bool gemv_dispatch(DArgs A, TaskP tp, char* ring, char* xb, float* red, Ctrl* c, CState& s, int cu,
-                              int w, int lane) {
+__device__ __forceinline__ bool gemv_dispatch(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
-  if (A->mfma) return gemv_task<1>(A, tp, ring, xb, red, c, s, cu, w, lane);
+  if (A->mfma) return gemv_task<0>(A, tp, cu, w, lane);
   switch (A->b) {
-    case 1: return gemv_task<1>(A, tp, ring, xb, red, c, s, cu, w, lane);
-    case 2: return gemv_task<2>(A, tp, ring, xb, red, c, s, cu, w, lane);
-    case 3: return gemv_task<3>(A, tp, ring, xb, red, c, s, cu, w, lane);
-    case 4: return gemv_task<4>(A, tp, ring, xb, red, c, s, cu, w, lane);
-    case 5: return gemv_task<5>(A, tp, ring, xb, red, c, s, cu, w, lane);
-    case 6: return gemv_task<6>(A, tp, ring, xb, red, c, s, cu, w, lane);
-    default: return gemv_task<7>(A, tp, ring, xb, red, c, s, cu, w, lane);
+    case 1: return gemv_task<1>(A, tp, cu, w, lane);
+    case 2: return gemv_task<2>(A, tp, cu, w, lane);
+    case 3: return gemv_task<3>(A, tp, cu, w, lane);
+    case 4: return gemv_task<4>(A, tp, cu, w, lane);
+    case 5: return gemv_task<5>(A, tp, cu, w, lane);
+    case 6: return gemv_task<6>(A, tp, cu, w, lane);
+    default: return gemv_task<7>(A, tp, cu, w, lane);
   }
 }
 
-__device__ void compute_main(DArgs A, char* ring, char* xb, float* red, Ctrl* c, int cu, int w, int lane) {
+__device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
   A = uni(A);
+  Ctrl* c = ctrl_block(A);
   const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
   const int nt = as_const(A->task_off)[cu + 1] - as_const(A->task_off)[cu];
-  CState s{0, 0, 0, 0, 0, 0, 0, 0, -1, -1, -1, -1, -1, -1, -1};
+  CState& s = c->cs[w];
+  s = CState{0, 0, 0, 0, 0, 0, 0, 0, -1, -1, -1, -1, -1, -1, -1};
   const uint64_t t_kernel0 = A->trace ? now_ticks() : 0;
   uint64_t* tr = (A->trace && w == 0 && lane == 0) ? A->trace + (size_t)cu * A->trace_cap * 4 : nullptr;
   const int rpc = 4096 / A->hd;
@@ -1371,27 +1529,26 @@ __device__ void compute_main(DArgs A, char* ring, char* xb, float* red, Ctrl* c,
     bool ok;
     int nch = 0;
     if (t.type == TT_GEMV) {
-      ok = gemv_dispatch(A, T + ti, ring, xb, red, c, s, cu, w, lane);
+      ok = gemv_dispatch(A, T + ti, cu, w, lane);
       nch = t.nchunks;
       had_lm = had_lm || t.stage == ST_LM;
     } else if (t.type == TT_ATTN) {
-      ok = A->hd == 128 ? attn_dispatch<128>(A, T + ti, ring, red, c, s, cu, w, lane)
-                        : attn_dispatch<64>(A, T + ti, ring, red, c, s, cu, w, lane);
-      nch = attn_task_chunks(A, c, cu, rpc);
+      ok = A->hd == 128 ? attn_dispatch<128>(A, T + ti, cu, w, lane) : attn_dispatch<64>(A, T + ti, cu, w, lane);
+      nch = attn_task_chunks(A, cu, rpc);
     } else {
-      ok = embed_task(A, T + ti, c, s, cu, w, lane);
+      ok = embed_task(A, T + ti, cu, w, lane);
     }
     if (!ok) return;
     s.q += nch;
     if (tr && ti < A->trace_cap) {
-      tr[ti * 4 + 0] = ((uint64_t)ti << 32) | ((uint64_t)t.type << 8) | (uint64_t)t.stage;
+      tr[ti * 4 + 0] = ((uint64_t)ti << 32) | ((uint64_t)(t.layer & 0xFFFF) << 16) | ((uint64_t)t.type << 8) | (uint64_t)t.stage;
       tr[ti * 4 + 1] = t_begin;
       tr[ti * 4 + 2] = t_dep;
       tr[ti * 4 + 3] = now_ticks();
     }
   }
   if (A->trace && lane == 0) {
-    uint64_t* st = A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * 32;
+    uint64_t* st = A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords;
     st[4 + w] = s.w_empty;
     st[8 + w] = s.w_bar;
     st[16 + w] = s.t_math;
@@ -1418,11 +1575,7 @@ __device__ void compute_main(DArgs A, char* ring, char* xb, float* red, Ctrl* c,
 __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
   (void)args;
   DArgs A = (DArgs)__builtin_amdgcn_kernarg_segment_ptr();
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* ring = lds;
-  char* xb = lds + (size_t)A->nslot * kChunkBytes;
-  float* red = (float*)(xb + A->xb_bytes);
-  Ctrl* c = (Ctrl*)((char*)red + kRedBytes);
+  Ctrl* c = ctrl_block(A);
   const int cu = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 
   // zero this CU's slice of the bank the next step will use
@@ -1436,6 +1589,8 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
     c->ready[tid] = 0;
     c->freed[tid] = 0;
   }
+  if (tid < kMaxBatch) c->lmkey[tid] = 0ull;
+  if (A->trace && tid < 16) A->trace[(size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32 + tid] = 0;
   if (tid == 0) {
     c->dep = 0;
     c->bar = 0;
@@ -1463,12 +1618,12 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
     if (st && cu == 0) atomicOr(A->status, st);
   }
   __syncthreads();
-  if (w < kComputeWaves) compute_main(A, ring, xb, red, c, cu, w, lane);
-  else loader_main(A, ring, c, cu, w - kComputeWaves, lane);
+  if (w < kComputeWaves) compute_main(A, cu, w, lane);
+  else loader_main(A, cu, w - kComputeWaves, lane);
 }
 
 size_t lds_bytes(int nslot, int xb_bytes) {
-  return (size_t)nslot * kChunkBytes + xb_bytes + kRedBytes + sizeof(Ctrl);
+  return (size_t)nslot * kChunkBytes + xb_bytes + kRedBytes + kCtrlBytes;
 }
 
 hipError_t launch_step(const DevArgs& A, hipStream_t stream) {

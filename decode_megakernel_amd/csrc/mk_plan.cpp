@@ -39,37 +39,58 @@ int stage_k(const PlanCfg& p, int st) {
   return 0;
 }
 
-// A GEMV stage is a grid of columns: (row group of `gs` 16-row sub-tiles) x
-// (512-wide K block).  Columns are dealt to CUs as equal contiguous ranges
-// ("stream-K"): a CU's range is split into tasks at row-group boundaries, and
-// a row group whose K range is split over several CUs is finished by the
-// last of its pieces.
+// A GEMV stage is tiled into 16-row sub-tiles over 512-wide K blocks, in one
+// of two ways:
+//  * row-owner: each CU owns a contiguous range of whole sub-tiles over the
+//    full K, cut into tasks of at most 4 x tiles_per_wave sub-tiles (wave w
+//    owns sub-tiles w, w+4, ...).  Nothing is split, so a task's epilogue
+//    runs straight from registers.
+//  * stream-K: columns = (row group of `gs` sub-tiles) x (K block) are dealt
+//    to CUs as equal contiguous ranges; a CU's range is cut into tasks at
+//    row-group boundaries, and a row group whose K range is split over
+//    several CUs is finished by the last of its pieces.
+// The cheaper one (chunks streamed by the busiest CU, a split charged as
+// kSplitChunks chunks of extra latency) is chosen per stage.
+constexpr int kSplitChunks = 6;
+
 struct Tiling {
-  int gs = 4;          // sub-tiles per group
+  bool owner = false;
+  int gs = 4;          // stream-K: sub-tiles per group
+  int tmax = 4;        // row-owner: sub-tiles per task
+  int nst = 1;         // sub-tiles of the stage
   int nkb = 1;         // K blocks
-  int ngroups = 1;
+  int ngroups = 1;     // stream-K groups
   long long ncols = 1;
 };
 
-Tiling tile_stage(const PlanCfg& p, int M, int K) {
-  const int st = (M + 15) / 16, nkb = (K + kKBlock - 1) / kKBlock;
+Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw) {
+  const int nst = (M + 15) / 16, nkb = (K + kKBlock - 1) / kKBlock;
   Tiling best;
+  best.nst = nst;
+  best.nkb = nkb;
   double best_cost = 1e300;
   for (int gs = kGroupSub; gs >= 1; gs >>= 1) {
-    Tiling t;
+    Tiling t = best;
     t.gs = gs;
-    t.nkb = nkb;
-    t.ngroups = (st + gs - 1) / gs;
+    t.ngroups = (nst + gs - 1) / gs;
     t.ncols = (long long)t.ngroups * nkb;
-    // chunks streamed by the busiest CU, plus a small per-task charge
     long long per_cu = (t.ncols + p.ncu - 1) / p.ncu;
-    double cost = (double)per_cu * gs + 0.25 * (double)per_cu / nkb + (gs < kGroupSub ? 0.01 : 0.0);
+    const bool split = (t.ncols % p.ncu) != 0 || ((t.ncols / p.ncu) % nkb) != 0;
+    double cost = (double)per_cu * gs + 0.25 * (double)per_cu / nkb + (gs < kGroupSub ? 0.01 : 0.0) +
+                  (split ? kSplitChunks : 0);
     if (cost < best_cost) {
       best_cost = cost;
       best = t;
     }
   }
-  return best;
+  Tiling own = best;
+  own.owner = true;
+  own.tmax = 4 * tpw;
+  const long long tiles_cu = (nst + p.ncu - 1) / p.ncu;
+  const long long tasks_cu = (tiles_cu + own.tmax - 1) / own.tmax;
+  const double own_cost = (double)tiles_cu * nkb + 0.25 * (double)tasks_cu;
+  const bool use_owner = p.gemv_mode == 1 || (p.gemv_mode == 0 && own_cost <= best_cost);
+  return use_owner ? own : best;
 }
 
 int owner(long long u, long long units, int ncu) { return (int)(u * ncu / units); }
@@ -132,10 +153,20 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   const int gemv_stages[5] = {ST_QKV, ST_O, ST_GU, ST_DOWN, ST_LM};
   // pieces of each group, identical for every layer of a stage
   std::vector<std::vector<int>> group_pieces(6);
+  const int tpw = tiles_per_wave(mfma ? 0 : batch);
   for (int si = 0; si < 5; ++si) {
     int st = gemv_stages[si];
-    tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st));
+    tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st), tpw);
     const Tiling& T = tl[st];
+    P.stage_owner[st] = T.owner ? 1 : 0;
+    if (T.owner) {
+      group_pieces[st].assign(1, 1);
+      grp_base[st] = grp_counters;
+      part_base[st] = part_blocks;
+      P.stage_ksplit[st] = 1;
+      P.stage_rows[st] = 16 * T.tmax;
+      continue;
+    }
     group_pieces[st].assign(T.ngroups, 0);
     for (int c = 0; c < ncu; ++c) {
       long long c0 = T.ncols * c / ncu, c1 = T.ncols * (c + 1) / ncu;
@@ -168,6 +199,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   std::vector<std::vector<int>> group_part(6);
   for (int si = 0; si < 5; ++si) {
     int st = gemv_stages[si];
+    if (tl[st].owner) continue;
     group_part[st].assign(tl[st].ngroups, -1);
     int nxt = part_base[st];
     for (int g = 0; g < tl[st].ngroups; ++g)
@@ -181,6 +213,28 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
     const int M = stage_rows(pc, st), K = stage_k(pc, st);
     const Tiling& T = tl[st];
     const int nst = (M + 15) / 16;
+    if (T.owner) {
+      for (int c = 0; c < ncu; ++c) {
+        const int t0 = (int)((long long)nst * c / ncu), t1 = (int)((long long)nst * (c + 1) / ncu);
+        if (t1 <= t0) continue;
+        const int n = t1 - t0, ntask = (n + T.tmax - 1) / T.tmax;
+        for (int k = 0; k < ntask; ++k) {
+          const int a = t0 + n * k / ntask, e = t0 + n * (k + 1) / ntask;
+          Task t = base_task(TT_GEMV, st, layer);
+          t.row0 = 16 * a;
+          t.nsub = e - a;
+          t.k0 = 0;
+          t.k1 = K;
+          t.wait_ctr = wait;
+          t.signal_ctr = signal;
+          t.nchunks = t.nsub * T.nkb;
+          cu_bytes[c] += (long long)std::min(16 * t.nsub, M - t.row0) * K * 2;
+          if (k == ntask - 1) t.flags |= kTaskSignal;
+          S[c].push_back(t);
+        }
+      }
+      return;
+    }
     std::vector<int> seen(T.ngroups, 0);
     for (int c = 0; c < ncu; ++c) {
       long long c0 = T.ncols * c / ncu, c1 = T.ncols * (c + 1) / ncu;
@@ -243,31 +297,39 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   }
 
   // ---- validation --------------------------------------------------------
-  // (1) every (row, K element) of every GEMV stage is covered exactly once,
-  //     the pieces of each group tile its K range in order, and chunk counts
-  //     match the tiling.
+  // (1) every (row, K element) of every GEMV stage is covered exactly once:
+  //     per sub-tile, the K ranges of the tasks covering it tile [0, K) in
+  //     piece order; split groups carry consistent piece indices; chunk
+  //     counts match the task shapes.
   for (int l = 0; l <= pc.L; ++l) {
     for (int si = 0; si < 5; ++si) {
       int st = gemv_stages[si];
       if ((st == ST_LM) != (l == pc.L)) continue;
       const Tiling& T = tl[st];
       const int M = stage_rows(pc, st), K = stage_k(pc, st);
-      std::vector<int> next_k(T.ngroups, 0), next_piece(T.ngroups, 0);
+      const int nst = (M + 15) / 16;
+      std::vector<int> next_k(nst, 0), pieces(nst, 0);
       long long covered = 0;
       for (int cu = 0; cu < ncu; ++cu)
         for (const Task& t : S[cu]) {
           if (t.type != TT_GEMV || t.stage != st || t.layer != l) continue;
-          int g = t.group;
-          if (g < 0 || g >= T.ngroups || t.row0 != g * 16 * T.gs) return MK_ERR_PLAN;
-          if (t.k0 != next_k[g] || t.k1 <= t.k0 || t.ks != next_piece[g]) return MK_ERR_PLAN;
-          if (t.k0 % kKBlock) return MK_ERR_PLAN;
-          next_k[g] = t.k1;
-          next_piece[g] += 1;
+          if (t.row0 % 16 || t.nsub < 1 || t.nsub > 4 * tpw || t.row0 / 16 + t.nsub > nst) return MK_ERR_PLAN;
+          if (t.k0 % kKBlock || t.k1 <= t.k0 || t.k1 > K) return MK_ERR_PLAN;
           if (t.nchunks != t.nsub * ((t.k1 - t.k0 + kKBlock - 1) / kKBlock)) return MK_ERR_PLAN;
+          if (T.owner && (t.nks != 1 || t.k0 != 0 || t.k1 != K)) return MK_ERR_PLAN;
+          if (!T.owner && (t.nsub > T.gs || t.row0 != t.group * 16 * T.gs || t.nks != group_pieces[st][t.group]))
+            return MK_ERR_PLAN;
+          for (int u = t.row0 / 16; u < t.row0 / 16 + t.nsub; ++u) {
+            if (t.k0 != next_k[u] || t.ks != pieces[u]) return MK_ERR_PLAN;
+            next_k[u] = t.k1;
+            pieces[u] += 1;
+          }
           covered += (long long)std::min(16 * t.nsub, M - t.row0) * (t.k1 - t.k0);
         }
-      for (int g = 0; g < T.ngroups; ++g)
-        if (next_k[g] != K || next_piece[g] != group_pieces[st][g]) return MK_ERR_PLAN;
+      for (int u = 0; u < nst; ++u) {
+        if (next_k[u] != K) return MK_ERR_PLAN;
+        if (!T.owner && pieces[u] != group_pieces[st][u / T.gs]) return MK_ERR_PLAN;
+      }
       if (covered != (long long)M * K) return MK_ERR_PLAN;
     }
   }

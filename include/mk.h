@@ -140,15 +140,18 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
 /* In-kernel trace (enabled when the environment variable MK_TRACE=<n> is set
  * at mk_create; otherwise *cap = 0 and nothing is copied).  Copies, enqueued
  * on `stream`, the trace of the last step into dst (device memory of at
- * least (n_cu*cap*4 + n_cu*32)*8 bytes): for each CU and each of its first
- * `cap` tasks, 4 uint64 words {task index << 32 | type << 8 | stage,
+ * least (n_cu*cap*4 + n_cu*64)*8 bytes): for each CU and each of its first
+ * `cap` tasks, 4 uint64 words {task index << 32 | layer << 16 | type << 8 | stage,
  * begin, dependency satisfied, end} in s_memrealtime ticks (100 MHz); then
- * 32 uint64 per CU: [0..3] ticks the loader waves waited for a free LDS
+ * 64 uint64 per CU: [0..3] ticks the loader waves waited for a free LDS
  * slot, [4..7] the compute waves waited for a loaded chunk, [8..11] the
  * compute waves waited in barriers, [12] compute wave 0's total time, [13]
  * loader wave 0's total time, [16..19] compute chunk math, [20..23] GEMV
- * input staging, [24..27] reductions and epilogues, [28..31] loader address
- * generation and load issue. */
+ * input staging, [24..27] reductions and epilogues; attention phases of
+ * compute wave 0 summed over layers: [32] query load and RoPE, [33] cached
+ * rows, [34] merge of the waves, [35] partial publish, [36] merge of a
+ * segment's partials, [37] output store, [38] completion signal, [39]
+ * pieces, [40] segments finished. */
 int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t* cap, void* stream);
 
 /* Synchronise `stream`, return the device status bits accumulated since the
