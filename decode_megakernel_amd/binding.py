@@ -187,7 +187,7 @@ class DecodeEngine:
         L = sh.n_layers
         spec = {STATE_HIDDEN: (L + 1, sh.hidden, torch.float32), STATE_HMID: (L, sh.hidden, torch.float32),
                 STATE_QKV: (L, sh.q_dim + 2 * sh.kv_dim, torch.float32),
-                STATE_ATTN: (L, sh.q_dim, torch.bfloat16), STATE_ACT: (L, sh.intermediate, torch.bfloat16)}
+                STATE_ATTN: (L, sh.q_dim, torch.float32), STATE_ACT: (L, sh.intermediate, torch.float32)}
         nl, width, dt = spec[which]
         out = torch.empty((nl, batch, width), dtype=dt, device="cuda")
         self.copy_state(which, batch, out)

@@ -57,7 +57,7 @@ struct mk_handle {
   size_t ws_bytes = 0;
   // workspace views
   float *hres, *hmid, *ssattn, *ssmlp, *qkv, *apart, *rope, *zero;
-  uint16_t *xattn, *xmlp, *attn_out, *act;
+  float *xattn, *xmlp, *attn_out, *act;
   uint32_t *banks, *seg_ctr, *status;
   int ctr_stride = 0, bank_words = 0;
   std::map<int, GraphDev> graphs;
@@ -178,7 +178,9 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   if (h->nslot < kLoaderWaves + 1) h->nslot = kLoaderWaves + 1;
   if (h->nslot > kMaxSlots) h->nslot = kMaxSlots;
   h->xb = xb_for((int)prop.sharedMemPerBlock, h->nslot);
-  if (h->xb < 4096) {
+  // the staging buffer holds attention's softmax states, and one 512-wide K
+  // block of every sequence's input as bf16 hi + lo halves (plus padding)
+  if (h->xb < kAttnStateBytes || h->xb < cfg->max_batch * (kKBlock + 8) * 4) {
     delete h;
     return MK_ERR_UNSUPPORTED;
   }
@@ -199,13 +201,13 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   };
   size_t o_hres = take((size_t)(L + 1) * bc * d * 4);
   size_t o_hmid = take((size_t)L * bc * d * 4);
-  size_t o_xattn = take((size_t)(L + 1) * bc * d * 2);
-  size_t o_xmlp = take((size_t)L * bc * d * 2);
+  size_t o_xattn = take((size_t)(L + 1) * bc * d * 4);
+  size_t o_xmlp = take((size_t)L * bc * d * 4);
   size_t o_ssattn = take((size_t)(L + 1) * (d / 16) * bc * 4);
   size_t o_ssmlp = take((size_t)L * (d / 16) * bc * 4);
   size_t o_qkv = take((size_t)L * bc * nqkv * 4);
-  size_t o_aout = take((size_t)L * bc * qdim * 2);
-  size_t o_act = take((size_t)L * bc * I * 2);
+  size_t o_aout = take((size_t)L * bc * qdim * 4);
+  size_t o_act = take((size_t)L * bc * I * 4);
   size_t o_apart = take((size_t)(h->ncu + bc * nkv) * kApartGroup * (hd + 4) * 4);
   size_t o_banks = take((size_t)2 * h->bank_words * 4);
   size_t o_seg = take((size_t)bc * nkv * 4);
@@ -224,13 +226,13 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   }
   h->hres = (float*)(h->ws + o_hres);
   h->hmid = (float*)(h->ws + o_hmid);
-  h->xattn = (uint16_t*)(h->ws + o_xattn);
-  h->xmlp = (uint16_t*)(h->ws + o_xmlp);
+  h->xattn = (float*)(h->ws + o_xattn);
+  h->xmlp = (float*)(h->ws + o_xmlp);
   h->ssattn = (float*)(h->ws + o_ssattn);
   h->ssmlp = (float*)(h->ws + o_ssmlp);
   h->qkv = (float*)(h->ws + o_qkv);
-  h->attn_out = (uint16_t*)(h->ws + o_aout);
-  h->act = (uint16_t*)(h->ws + o_act);
+  h->attn_out = (float*)(h->ws + o_aout);
+  h->act = (float*)(h->ws + o_act);
   h->apart = (float*)(h->ws + o_apart);
   h->banks = (uint32_t*)(h->ws + o_banks);
   h->seg_ctr = (uint32_t*)(h->ws + o_seg);
@@ -439,8 +441,8 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
     case MK_STATE_HIDDEN: src = h->hres; width = c.hidden; layers = c.n_layers + 1; break;
     case MK_STATE_HMID: src = h->hmid; width = c.hidden; break;
     case MK_STATE_QKV: src = h->qkv; width = nqkv; break;
-    case MK_STATE_ATTN: src = h->attn_out; width = qdim; esize = 2; break;
-    case MK_STATE_ACT: src = h->act; width = c.intermediate; esize = 2; break;
+    case MK_STATE_ATTN: src = h->attn_out; width = qdim; esize = 4; break;
+    case MK_STATE_ACT: src = h->act; width = c.intermediate; esize = 4; break;
     default: return MK_ERR_INVALID_ARG;
   }
   const size_t row = (size_t)batch * width * esize, spitch = (size_t)c.max_batch * width * esize;

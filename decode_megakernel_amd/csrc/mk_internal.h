@@ -26,11 +26,12 @@ constexpr int kMaxBatch = 16;
 constexpr int kMaxGroup = 8;                 // n_q / n_kv
 constexpr int kKBlock = 512;                 // K elements per chunk (64 lanes x 8 for VALU, 16 MFMA k-steps)
 constexpr int kGroupSub = 4;                 // 16-row sub-tiles per row group (one per compute wave)
-// LDS for cross-wave reductions: GEMV partial tiles (4 waves x 4 KB) or two
-// piece-parity buffers of attention states (4 waves x group x (head_dim + 4)
-// floats), whichever is larger for group <= 4 at head_dim 128 and group <= 8
-// at head_dim 64.
-constexpr int kRedBytes = 2 * 4 * 8 * (64 + 4) * 4;
+// LDS for the GEMV tile reductions: one 16-row x 16-sequence fp32 tile per
+// compute wave.  Attention keeps its per-wave softmax states in the GEMV
+// input staging buffer instead (the two never run at once), which needs
+// kAttnStateBytes of it.
+constexpr int kRedBytes = 4 * 256 * 4;
+constexpr int kAttnStateBytes = 2 * 4 * 8 * (64 + 4) * 4;  // 2 piece parities x 4 waves x group x (hd + 4) fp32
 constexpr int kStatWords = 64;               // trace: per-CU phase totals (uint64 words)
 constexpr int kCtrlBytes = 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
 constexpr int kApartGroup = 8;               // group slots per attention partial
@@ -118,13 +119,13 @@ struct DevArgs {
   int32_t bcap;         // workspace batch capacity
   float* hres;          // [L+1][bcap][d]
   float* hmid;          // [L][bcap][d]
-  uint16_t* xattn;      // [L+1][bcap][d]  bf16(h * norm weight): GEMV input of QKV / LM head
-  uint16_t* xmlp;       // [L][bcap][d]    bf16(h_mid * norm weight): GEMV input of gate/up
+  float* xattn;         // [L+1][bcap][d]  h * norm weight: GEMV input of QKV / LM head
+  float* xmlp;          // [L][bcap][d]    h_mid * norm weight: GEMV input of gate/up
   float* ssattn;        // [L+1][d/16][bcap] partial sums of squares per 16-row tile
   float* ssmlp;         // [L][d/16][bcap]
   float* qkv;           // [L][bcap][nqkv]
-  uint16_t* attn_out;   // [L][bcap][qdim]
-  uint16_t* act;        // [L][bcap][I]
+  float* attn_out;      // [L][bcap][qdim] attention output: GEMV input of O
+  float* act;           // [L][bcap][I]    silu(gate) * up: GEMV input of down
   float* part;          // split-K partial blocks, 1024 floats each
   float* apart;         // attention partials [ncu + bcap*nkv][group][hd + 4]
   uint32_t* banks;      // 2 banks of kShards * ctr_stride words, then keys

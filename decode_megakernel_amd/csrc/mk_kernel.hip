@@ -133,6 +133,24 @@ __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
   f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
 }
 
+// Split 8 fp32 values into bf16 pairs hi + lo: hi is x truncated to bf16
+// (exact), lo the bf16 rounding of the exact remainder x - hi, so hi + lo
+// carries x to a relative 2^-17.  Two bf16 dot products (or MFMAs) then
+// multiply a bf16 weight by an almost-fp32 activation.
+__device__ __forceinline__ void split8(u32x4 a, u32x4 b, u32x4& hi, u32x4& lo) {
+  const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x0 = x[2 * i], x1 = x[2 * i + 1];
+    const uint32_t h0 = x0 & 0xFFFF0000u, h1 = x1 & 0xFFFF0000u;
+    h[i] = (h0 >> 16) | h1;
+    r[i] = f2bf(__uint_as_float(x0) - __uint_as_float(h0)) | (f2bf(__uint_as_float(x1) - __uint_as_float(h1)) << 16);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{r[0], r[1], r[2], r[3]};
+}
+
 // LDS accessors
 __device__ __forceinline__ u32x4 lds_ld16(const char* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void lds_st16(char* p, u32x4 v) { *(u32x4*)p = v; }
@@ -288,7 +306,7 @@ __device__ __forceinline__ int stage_K(DArgs A, int st) {
   }
 }
 // bf16 input activation [bcap][K] of a GEMV stage
-__device__ __forceinline__ const uint16_t* stage_x(DArgs A, int st, int l) {
+__device__ __forceinline__ const float* stage_x(DArgs A, int st, int l) {
   switch (st) {
     case ST_QKV: return A->xattn + (size_t)l * A->bcap * A->d;
     case ST_O: return A->attn_out + (size_t)l * A->bcap * A->qdim;
@@ -744,16 +762,21 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == kk0 && s.x_k1 == kk1) return true;
   // every compute wave must be done reading the previous slice
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  // the fp32 input slice as bf16 hi and lo halves: [n][ksp] hi, then [n][ksp] lo
   const int K = stage_K(A, t.stage);
   const int ksl = kk1 - kk0, ksp = ksl + 8;
-  const uint16_t* x = stage_x(A, t.stage, t.layer);
+  const float* x = stage_x(A, t.stage, t.layer);
+  char* xlo = xb + (size_t)A->b * ksp * 2;
   const int per_row = ksl / 8;
   const int units = A->b * per_row;
   const int tid = w * 64 + lane;
   for (int u = tid; u < units; u += kComputeThreads) {
     int n = u / per_row, kq = u - n * per_row;
-    u32x4 v = co_load16(x, (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 2));
-    lds_st16(xb + ((size_t)n * ksp + 8 * kq) * 2, v);
+    const uint32_t off = (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 4);
+    u32x4 hi, lo;
+    split8(co_load16(x, off), co_load16(x, off + 16), hi, lo);
+    lds_st16(xb + ((size_t)n * ksp + 8 * kq) * 2, hi);
+    lds_st16(xlo + ((size_t)n * ksp + 8 * kq) * 2, lo);
   }
   const float* ss = stage_ss(A, t.stage, t.layer);
   if (ss && !(s.r_stage == t.stage && s.r_layer == t.layer)) {
@@ -775,18 +798,22 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
 }
 
 // ---- VALU chunk: 16 rows x 512 K; lane l covers K elements [8l, 8l+8)
+//      (input as bf16 hi + lo halves, xlo_off bytes apart in LDS)
 template <int NB>
-__device__ __forceinline__ void valu_chunk(const char* slot, const char* xb, int ksp, int kl, int klen, int lane,
-                                           float (&acc)[16][NB]) {
-  u32x4 xv[NB];
+__device__ __forceinline__ void valu_chunk(const char* slot, const char* xb, int xlo_off, int ksp, int kl, int klen,
+                                           int lane, float (&acc)[16][NB]) {
+  u32x4 xh[NB], xl[NB];
   const bool ok = kl < klen;
 #pragma unroll
-  for (int n = 0; n < NB; ++n) xv[n] = ok ? lds_ld16(xb + ((size_t)n * ksp + kl) * 2) : u32x4{0, 0, 0, 0};
+  for (int n = 0; n < NB; ++n) {
+    xh[n] = ok ? lds_ld16(xb + ((size_t)n * ksp + kl) * 2) : u32x4{0, 0, 0, 0};
+    xl[n] = ok ? lds_ld16(xb + xlo_off + ((size_t)n * ksp + kl) * 2) : u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     u32x4 wv = lds_ld16(slot + j * 1024 + lane * 16);
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[j][n] = dot8_bf16(wv, xv[n], acc[j][n]);
+    for (int n = 0; n < NB; ++n) acc[j][n] = dot8_bf16(wv, xh[n], dot8_bf16(wv, xl[n], acc[j][n]));
   }
 }
 
@@ -829,16 +856,21 @@ __device__ __forceinline__ void valu_reduce(float (&acc)[16][NB], int lane, floa
 
 // ---- MFMA chunk: one 16-row sub-tile x 16 k-steps of 32; B operand (the
 //      input, batch padded to 16 with zeros) from the staged LDS slice.
-__device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int ksp, int kl, int klen, int b, int lane,
-                                           f32x4& acc) {
+//      The input is bf16 hi + lo halves (xlo_off bytes apart): two MFMAs per
+//      k-step into the same accumulator.
+__device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int xlo_off, int ksp, int kl, int klen, int b,
+                                           int lane, f32x4& acc) {
   const int n = lane & 15, kq = 8 * (lane >> 4);
 #pragma unroll
   for (int s = 0; s < kWaveLoads; ++s) {
     if (kl + 32 * s >= klen) break;
     const int k = kl + 32 * s + kq;
-    u32x4 bv = n < b ? lds_ld16(xb + ((size_t)n * ksp + k) * 2) : u32x4{0, 0, 0, 0};
+    u32x4 bh = n < b ? lds_ld16(xb + ((size_t)n * ksp + k) * 2) : u32x4{0, 0, 0, 0};
+    u32x4 bl = n < b ? lds_ld16(xb + xlo_off + ((size_t)n * ksp + k) * 2) : u32x4{0, 0, 0, 0};
     u32x4 av = lds_ld16(slot + s * 1024 + lane * 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bl),
+                                                  acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bh),
                                                   acc, 0, 0, 0);
   }
 }
@@ -862,16 +894,15 @@ __device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, i
       // per-16-row sum of squares.
       const bool down = t.stage == ST_DOWN;
       float* hout = down ? A->hres + (size_t)(l + 1) * A->bcap * A->d : A->hmid + (size_t)l * A->bcap * A->d;
-      uint16_t* xo = down ? A->xattn + (size_t)(l + 1) * A->bcap * A->d : A->xmlp + (size_t)l * A->bcap * A->d;
+      float* xo = down ? A->xattn + (size_t)(l + 1) * A->bcap * A->d : A->xmlp + (size_t)l * A->bcap * A->d;
       const uint16_t* nw = down ? (l + 1 < A->L ? as_const(A->layers)[l + 1].attn_norm : A->final_norm) : as_const(A->layers)[l].mlp_norm;
       float* ssout = down ? A->ssattn + (size_t)(l + 1) * (A->d / 16) * A->bcap : A->ssmlp + (size_t)l * (A->d / 16) * A->bcap;
       const uint32_t off = (uint32_t)(((size_t)n * A->d + lr) * 4);
       float h = valid ? resid + val : 0.f;
-      float xn = valid ? h * bf2f(nw[lr]) : 0.f;
-      float xn_next = __shfl_down(xn, 1);
+      const float xn = valid ? h * bf2f(nw[lr]) : 0.f;
       if (valid) {
         co_storef(hout, off, h);
-        if ((row & 1) == 0) co_store4(xo, (uint32_t)(((size_t)n * A->d + lr) * 2), pack_bf2(xn, xn_next));
+        co_storef(xo, off, xn);
       }
       float ss = sum16(h * h);
       if (valid && row == 0) co_storef(ssout, (uint32_t)((((size_t)lr >> 4) * A->bcap + n) * 4), ss);
@@ -884,10 +915,9 @@ __device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, i
         float g = c->rms[n] * val, u = c->rms[n] * val_up;
         a = g / (1.0f + __expf(-g)) * u;
       }
-      float a_next = __shfl_down(a, 1);
-      if (valid && row < 8 && (row & 1) == 0) {
+      if (valid && row < 8) {
         const int out = 8 * (lr >> 4) + row;
-        co_store4(A->act, (uint32_t)((((size_t)l * A->bcap + n) * A->I + out) * 2), pack_bf2(a, a_next));
+        co_storef(A->act, (uint32_t)((((size_t)l * A->bcap + n) * A->I + out) * 4), a);
       }
       break;
     }
@@ -955,7 +985,8 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       for (int n = 0; n < NV; ++n) vacc[i][j][n] = 0.f;
   }
   // K windows that fit the LDS staging buffer
-  int wkb = ((A->xb_bytes / (2 * A->b)) - 8) / kKBlock;
+  // (4 bytes per staged element: bf16 hi + lo)
+  int wkb = ((A->xb_bytes / (4 * A->b)) - 8) / kKBlock;
   if (wkb < 1) wkb = 1;
   for (int wb = 0; wb < nkb; wb += wkb) {
     const int we = min(nkb, wb + wkb);
@@ -963,7 +994,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     const uint64_t ts0 = A->trace ? now_ticks() : 0;
     if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane)) return false;
     if (A->trace) s.t_stage += now_ticks() - ts0;
-    const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0;
+    const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0, xlo_off = A->b * ksp * 2;
     for (int kb = wb; kb < we && nown > 0; ++kb) {
       const int kl = (kb - wb) * kKBlock;
 #pragma unroll
@@ -973,8 +1004,8 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
         if (!wait_chunk(A, c, gq, s.w_empty)) return false;
         const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
         const uint64_t tm0 = A->trace ? now_ticks() : 0;
-        if constexpr (NB > 0) valu_chunk<NB>(slot, xb, ksp, kl + 8 * lane, klen, lane, vacc[i]);
-        else mfma_chunk(slot, xb, ksp, kl, klen, A->b, lane, macc[i]);
+        if constexpr (NB > 0) valu_chunk<NB>(slot, xb, xlo_off, ksp, kl + 8 * lane, klen, lane, vacc[i]);
+        else mfma_chunk(slot, xb, xlo_off, ksp, kl, klen, A->b, lane, macc[i]);
         free_chunk(A, c, gq, lane);
         if (A->trace) s.t_math += now_ticks() - tm0;
       }
@@ -983,7 +1014,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   const uint64_t te0 = A->trace ? now_ticks() : 0;
   // owned sub-tile i's totals -> this wave's LDS scratch as [16 rows][16 n],
   // read back with lanes mapped to (row = lane & 15, n = lane / 16 + 4 j)
-  float* rw = red + w * 1024;
+  float* rw = red + w * 256;
   auto tile_values = [&](int i, float (&val)[4], float (&up)[4]) {
     if constexpr (NB > 0) {
       float tot[NB];
@@ -1097,8 +1128,9 @@ __device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int la
     const uint16_t* nw = as_const(A->layers)[0].attn_norm + col;
     co_store16(A->hres, (uint32_t)(((size_t)n * A->d + col) * 4),
                u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
-    co_store8(A->xattn, (uint32_t)(((size_t)n * A->d + col) * 2),
-              u32x2{pack_bf2(h[0] * bf2f(nw[0]), h[1] * bf2f(nw[1])), pack_bf2(h[2] * bf2f(nw[2]), h[3] * bf2f(nw[3]))});
+    co_store16(A->xattn, (uint32_t)(((size_t)n * A->d + col) * 4),
+               u32x4{__float_as_uint(h[0] * bf2f(nw[0])), __float_as_uint(h[1] * bf2f(nw[1])),
+                     __float_as_uint(h[2] * bf2f(nw[2])), __float_as_uint(h[3] * bf2f(nw[3]))});
   }
   float ss = h[0] * h[0] + h[1] * h[1] + h[2] * h[2] + h[3] * h[3];
   ss += __shfl_xor(ss, 1);
@@ -1154,7 +1186,8 @@ template <int HD, int GM>
 __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
   char* ring = mk_lds;
-  float* red = red_scratch(A);
+  // per-wave softmax states live in the GEMV staging buffer while attention runs
+  float* red = (float*)xb_stage(A);
   Ctrl* c = ctrl_block(A);
   CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
@@ -1341,7 +1374,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     const int npieces = W >= A->ncu ? c_last - c_first + 1
                                    : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
     const int pstride = GM * (HD + 4);
-    uint16_t* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
+    float* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
     if (w == 0) {
       // merge the 4 wave states (lane group 0 holds 8 elements per lane)
       const float* s0 = red + (pidx & 1) * stride_st;
@@ -1373,9 +1406,12 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
           for (int h = 0; h < GM; ++h) {
             if (h >= G) continue;
             const float inv = 1.0f / Lsum[h];
-            co_store16(ob, (uint32_t)((h * HD + e0) * 2),
-                       u32x4{pack_bf2(O[h][0] * inv, O[h][1] * inv), pack_bf2(O[h][2] * inv, O[h][3] * inv),
-                             pack_bf2(O[h][4] * inv, O[h][5] * inv), pack_bf2(O[h][6] * inv, O[h][7] * inv)});
+            co_store16(ob, (uint32_t)((h * HD + e0) * 4),
+                       u32x4{__float_as_uint(O[h][0] * inv), __float_as_uint(O[h][1] * inv),
+                             __float_as_uint(O[h][2] * inv), __float_as_uint(O[h][3] * inv)});
+            co_store16(ob, (uint32_t)((h * HD + e0 + 4) * 4),
+                       u32x4{__float_as_uint(O[h][4] * inv), __float_as_uint(O[h][5] * inv),
+                             __float_as_uint(O[h][6] * inv), __float_as_uint(O[h][7] * inv)});
           }
         }
       } else {
@@ -1456,8 +1492,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
           }
           if (sub == 0) {
             const float inv = 1.0f / lsum;
-            co_store8(ob, (uint32_t)((h * HD + el) * 2),
-                      u32x2{pack_bf2(acc[0] * inv, acc[1] * inv), pack_bf2(acc[2] * inv, acc[3] * inv)});
+            co_store16(ob, (uint32_t)((h * HD + el) * 4),
+                       u32x4{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
+                             __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)});
           }
         }
         mark(4);
@@ -1472,6 +1509,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   mark(6);
+  s.x_stage = -1;  // the staging buffer held softmax states
   return true;
 }
 

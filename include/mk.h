@@ -127,8 +127,8 @@ int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream);
  *   MK_STATE_HIDDEN   float, L+1 layers, width hidden (same as mk_copy_hidden)
  *   MK_STATE_HMID     float, L, hidden: residual after attention + O proj
  *   MK_STATE_QKV      float, L, (n_q+2 n_kv) head_dim: raw q|k|v projections
- *   MK_STATE_ATTN     bf16,  L, n_q head_dim: attention output per head
- *   MK_STATE_ACT      bf16,  L, intermediate: silu(gate) * up
+ *   MK_STATE_ATTN     fp32,  L, n_q head_dim: attention output per head
+ *   MK_STATE_ACT      fp32,  L, intermediate: silu(gate) * up
  * Returns MK_ERR_INVALID_ARG for an unknown `which`. */
 #define MK_STATE_HIDDEN 0
 #define MK_STATE_HMID 1
