@@ -111,21 +111,29 @@ def cpu_baseline(wl, S, host_sample_layers=None):
     W = oracle.Weights(sub, bits, keep=False)
     kv = oracle.KVState(sub, kbits, vbits, S["ctx"])
     toks = [int(t) for t in S["tok"][0].cpu()]
-    t0 = time.perf_counter()
-    x = W.rows("model.embed_tokens.weight", np.asarray(toks))
     pos = S["ctx"]
-    for l in range(nl):
-        x, *_ = oracle.layer_forward(sub, W, l, x, pos, lambda i, l=l: kv.rows(l, i, pos[i]))
-    t_layers = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    oracle.lm_head(sub, W, x)
-    t_head = time.perf_counter() - t1
-    step_s = t_layers * (L / nl) + t_head
-    sample = (f"one full float64 oracle decode step (batch {b})" if nl == L else
-              f"{nl} of {L} layers plus the LM head of one float64 oracle decode step (batch {b}), "
-              f"layer time scaled to {L} layers")
+    # repeat the sampled step until about 10 s of CPU work (at most 30 s)
+    t_layers = t_head = 0.0
+    reps = 0
+    while reps == 0 or (t_layers + t_head < 10.0 and reps < 200):
+        t0 = time.perf_counter()
+        x = W.rows("model.embed_tokens.weight", np.asarray(toks))
+        for l in range(nl):
+            x, *_ = oracle.layer_forward(sub, W, l, x, pos, lambda i, l=l: kv.rows(l, i, pos[i]))
+        t1 = time.perf_counter()
+        oracle.lm_head(sub, W, x)
+        t2 = time.perf_counter()
+        t_layers += t1 - t0
+        t_head += t2 - t1
+        reps += 1
+        if t_layers + t_head > 30.0:
+            break
+    step_s = (t_layers * (L / nl) + t_head) / reps
+    sample = (f"{reps} repetitions of one full float64 oracle decode step (batch {b})" if nl == L else
+              f"{reps} repetitions of {nl} of {L} layers plus the LM head of one float64 oracle decode step "
+              f"(batch {b}), layer time scaled to {L} layers")
     return {"value": b / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "sample": sample,
-            "seconds_measured": round(t_layers + t_head, 3)}
+            "seconds_measured": round(t_layers + t_head, 3), "repetitions": reps}
 
 
 def traffic_from_profile(workload):

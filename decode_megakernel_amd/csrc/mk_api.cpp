@@ -91,6 +91,8 @@ static int check_cfg(const mk_model_cfg* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return MK_ERR_UNSUPPORTED;
   if (G > (c->head_dim == 128 ? 4 : 8)) return MK_ERR_UNSUPPORTED;
   if (c->hidden % 64 || c->intermediate % 64) return MK_ERR_UNSUPPORTED;
+  // the input staging sums at most 512 per-16-row partial sums of squares
+  if (c->hidden > 8192) return MK_ERR_UNSUPPORTED;
   // a K slice of one row of 16 bf16 columns per sequence must fit the staging buffer
   return MK_OK;
 }

@@ -19,6 +19,14 @@
 
 #include "mk_internal.h"
 
+// Per-phase timers of the in-kernel trace (per-CU stats words 32..61).  They
+// cost registers in the task functions, so they are compiled only into
+// analysis builds (-DMK_PHASE_TRACE=1); the per-task timestamps and the
+// wait totals are always available.
+#ifndef MK_PHASE_TRACE
+#define MK_PHASE_TRACE 0
+#endif
+
 namespace mk {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -416,8 +424,15 @@ __device__ __forceinline__ long long attn_total(const Ctrl* c, int b, int nkv) {
   for (int i = 0; i < b; ++i) W += c->slen[i];
   return W * nkv;
 }
-__device__ __forceinline__ long long cu_lo(int cu, long long W, int ncu) { return W * cu / ncu; }
+// First flattened row of CU cu's range, and the CU holding row x.  32-bit
+// divisions when W * ncu fits (the common case), 64-bit otherwise.
+__device__ __forceinline__ long long cu_lo(int cu, long long W, int ncu) {
+  if ((unsigned long long)W * (unsigned)ncu <= 0xFFFFFFFFull) return (long long)((uint32_t)W * (uint32_t)cu / (uint32_t)ncu);
+  return W * cu / ncu;
+}
 __device__ __forceinline__ int cu_of(long long x, long long W, int ncu) {
+  if ((unsigned long long)W * (unsigned)ncu + (unsigned long long)W <= 0xFFFFFFFFull)
+    return (int)(((uint32_t)(x + 1) * (uint32_t)ncu + (uint32_t)W - 1u) / (uint32_t)W) - 1;
   return (int)(((x + 1) * ncu + W - 1) / W) - 1;
 }
 
@@ -720,11 +735,18 @@ __device__ __forceinline__ void free_chunk(DArgs A, Ctrl* c, int gq, int lane) {
 // DPP lane moves within 16-lane rows: quad_perm [1,0,3,2] (lane ^ 1),
 // quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (lane i of each 8 <- 7-i),
 // row_mirror (lane i of each 16 <- 15-i), row_ror:8 (lane ^ 8).
+// A DPP move reads other lanes' registers, so it must run with every lane of
+// the wave active.  Callers use its result unconditionally (never as one arm
+// of a select: the compiler may turn that into a branch, and a move reading
+// a lane switched off by the branch returns 0).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppRor8 = 0x128;
+// row_ror:n moves lane (i - n) mod 16 of each row into lane i; row_shl:n
+// moves lane i + n and row_shr:n lane i - n (0 past the row's ends).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppShl4 = 0x104,
+              kDppShr4 = 0x114, kDppRor8 = 0x128;
 // Sum over aligned groups of N lanes (N = 2, 4, 8 or 16); every lane of a
 // group gets the group's total.
 template <int N>
@@ -784,7 +806,9 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
     for (int n = w; n < A->b; n += kComputeWaves) {
       float acc = 0.f;
       for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4));
-      for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+      acc = group_sum<16>(acc);
+      acc += __shfl_xor(acc, 16);
+      acc += __shfl_xor(acc, 32);
       if (lane == 0) c->rms[n] = 1.0f / sqrtf(acc / (float)A->d + A->eps);
     }
     s.r_stage = t.stage;
@@ -841,15 +865,21 @@ __device__ __forceinline__ void valu_reduce(float (&acc)[16][NB], int lane, floa
     for (int r = 0; r < 2; ++r) {
       float send = b3 ? v4[r] : v4[r + 2];
       float keep = b3 ? v4[r + 2] : v4[r];
-      v2[r] = keep + __shfl_xor(send, 8);
+      v2[r] = keep + dpp_f<kDppRor8>(send);  // lane ^ 8
     }
     {
       float send = b2 ? v2[0] : v2[1];
       float keep = b2 ? v2[1] : v2[0];
-      v1 = keep + __shfl_xor(send, 4);
+      // lane ^ 4 within a 16-lane row: lanes with bit 2 clear read lane + 4,
+      // the others lane - 4.  Both moves run on every lane with the unwanted
+      // direction zeroed at the source (a select between two moved values
+      // may be turned into a branch, and a move that reads a lane switched
+      // off by the branch returns 0).
+      const float s_up = b2 ? send : 0.f, s_dn = b2 ? 0.f : send;
+      v1 = keep + dpp_f<kDppShl4>(s_up) + dpp_f<kDppShr4>(s_dn);
     }
-    v1 += __shfl_xor(v1, 2);
-    v1 += __shfl_xor(v1, 1);
+    v1 += dpp_f<kDppXor2>(v1);
+    v1 += dpp_f<kDppXor1>(v1);
     out[n] = v1;
   }
 }
@@ -974,6 +1004,19 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       const int n = (lane >> 4) + 4 * j, lr = t.row0 + 16 * (w + kComputeWaves * i) + row;
       if (has_resid && i < nown && n < A->b && lr < M) resid[i][j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4));
     }
+  // trace: GEMV phase totals of compute wave 0, per stage (per-CU stats words
+  // 42 + 4 * stage + {0 staging, 1 chunks, 2 reduce + epilogue, 3 signal})
+  uint64_t* gst = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0)
+                      ? A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 42 + 4 * (t.stage == ST_LM ? 1 : t.stage)
+                      : nullptr;
+  uint64_t gt = gst ? now_ticks() : 0;
+  auto gmark = [&](int k) {
+    if (gst) {
+      const uint64_t tn = now_ticks();
+      gst[k] += tn - gt;
+      gt = tn;
+    }
+  };
   float vacc[TPW][16][NV];
   f32x4 macc[TPW];
 #pragma unroll
@@ -994,6 +1037,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     const uint64_t ts0 = A->trace ? now_ticks() : 0;
     if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane)) return false;
     if (A->trace) s.t_stage += now_ticks() - ts0;
+    gmark(0);
     const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0, xlo_off = A->b * ksp * 2;
     for (int kb = wb; kb < we && nown > 0; ++kb) {
       const int kl = (kb - wb) * kKBlock;
@@ -1012,6 +1056,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     }
   }
   const uint64_t te0 = A->trace ? now_ticks() : 0;
+  gmark(1);
   // owned sub-tile i's totals -> this wave's LDS scratch as [16 rows][16 n],
   // read back with lanes mapped to (row = lane & 15, n = lane / 16 + 4 j)
   float* rw = red + w * 256;
@@ -1094,6 +1139,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], lane);
     }
   }
+  gmark(2);
   if (t.flags & kTaskSignal) {
     wait_mem();
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
@@ -1107,6 +1153,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       if (lane == 0) signal_counter(A, t.signal_ctr, cu);
     }
   }
+  gmark(3);
   if (A->trace) s.t_epi += now_ticks() - te0;
   return true;
 }
@@ -1202,7 +1249,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   const MK_AS4 LayerW& lw = as_const(A->layers)[l];
   const int stride_st = kComputeWaves * GM * (HD + 4);
   // trace: attention phase totals of compute wave 0 (per-CU stats words 32..40)
-  uint64_t* ast = (A->trace && w == 0 && lane == 0)
+  uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0)
                       ? A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32
                       : nullptr;
   uint64_t tlast = ast ? now_ticks() : 0;
@@ -1239,9 +1286,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     for (int ch = 0; ch < P.nch; ++ch) {
       const int gq = qc + ch;
       if ((gq & (kComputeWaves - 1)) != w) continue;
-      const uint64_t tw0 = ast ? now_ticks() : 0;
+      const uint64_t tw0 = MK_PHASE_TRACE && ast ? now_ticks() : 0;
       if (!wait_chunk(A, c, gq, s.w_empty)) return false;
-      if (ast) ast[9] += now_ticks() - tw0;
+      if (MK_PHASE_TRACE && ast) ast[9] += now_ticks() - tw0;
       const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
       const int rows = min(RPC, P.ncached - ch * RPC);
       // scores of every row of the chunk first (lane group gi holds rows
@@ -1267,8 +1314,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         float mx = -INFINITY;
 #pragma unroll
         for (int pass = 0; pass < NP; ++pass) {
-          const float v = group_sum<LPR>(sc[h][pass]);
-          sc[h][pass] = pass * RP + gi < rows ? v : -INFINITY;
+          // rows past the chunk's end get -inf added (the sum itself is
+          // always used, see dpp_f)
+          sc[h][pass] = group_sum<LPR>(sc[h][pass]) + (pass * RP + gi < rows ? 0.f : -INFINITY);
           mx = fmaxf(mx, sc[h][pass]);
         }
         const float mn = fmaxf(st[h].m, mx);
@@ -1628,7 +1676,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
     c->freed[tid] = 0;
   }
   if (tid < kMaxBatch) c->lmkey[tid] = 0ull;
-  if (A->trace && tid < 16) A->trace[(size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32 + tid] = 0;
+  if (A->trace && tid < 32) A->trace[(size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32 + tid] = 0;
   if (tid == 0) {
     c->dep = 0;
     c->bar = 0;

@@ -151,7 +151,10 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
  * compute wave 0 summed over layers: [32] query load and RoPE, [33] cached
  * rows, [34] merge of the waves, [35] partial publish, [36] merge of a
  * segment's partials, [37] output store, [38] completion signal, [39]
- * pieces, [40] segments finished. */
+ * pieces, [40] segments finished, [41] waits for cached rows; GEMV phases of
+ * compute wave 0 summed over layers, at [42 + 4 s + k] for stage s (QKV 0,
+ * LM head 1, O 2, gate/up 3, down 4) and k = 0 input staging, 1 streamed
+ * chunks, 2 reductions and epilogue, 3 completion signal. */
 int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t* cap, void* stream);
 
 /* Synchronise `stream`, return the device status bits accumulated since the
