@@ -31,7 +31,14 @@ constexpr int kGroupSub = 4;                 // 16-row sub-tiles per row group (
 // input staging buffer instead (the two never run at once), which needs
 // kAttnStateBytes of it.
 constexpr int kRedBytes = 4 * 256 * 4;
-constexpr int kAttnStateBytes = 2 * 4 * 8 * (64 + 4) * 4;  // 2 piece parities x 4 waves x group x (hd + 4) fp32
+// attention's use of the staging buffer (largest over head_dim 64 / group 8
+// and head_dim 128 / group 4): wave states (2 piece parities x 4 waves x
+// group x (hd + 4) fp32), per-wave queries (group x hd) and probabilities
+// (rows per chunk x 4 or 8 heads)
+constexpr int kAttnStateBytes =
+    (2 * 4 * 8 * (64 + 4) + 4 * 8 * 64 + 4 * 64 * 8) * 4 > (2 * 4 * 4 * (128 + 4) + 4 * 4 * 128 + 4 * 32 * 4) * 4
+        ? (2 * 4 * 8 * (64 + 4) + 4 * 8 * 64 + 4 * 64 * 8) * 4
+        : (2 * 4 * 4 * (128 + 4) + 4 * 4 * 128 + 4 * 32 * 4) * 4;
 constexpr int kStatWords = 64;               // trace: per-CU phase totals (uint64 words)
 constexpr int kCtrlBytes = 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
 constexpr int kApartGroup = 8;               // group slots per attention partial

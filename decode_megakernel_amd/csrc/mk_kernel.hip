@@ -93,6 +93,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
 __device__ __forceinline__ u32x4 co_load16(const void* base, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), off, 0, kCpSc1);
 }
+__device__ __forceinline__ u32x2 co_load8(const void* base, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rsrc(base), off, 0, kCpSc1);
+}
 __device__ __forceinline__ uint32_t co_load4(const void* base, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(rsrc(base), off, 0, kCpSc1);
 }
@@ -1229,26 +1232,45 @@ __device__ __forceinline__ void rope_head(DArgs A, const float* src /* head base
   }
 }
 
+// One attention task: this CU's range of the flattened (sequence, KV head,
+// position) rows, as pieces that each lie inside one (sequence, KV head)
+// segment.  Scores of a chunk come from MFMAs (the group's query heads as A,
+// bf16 hi + lo halves; the chunk's K rows as B), the softmax state (m, l) per
+// head is wave-uniform with one rescale per chunk, and V is accumulated on
+// the VALU with each lane group holding 8 dimensions of its rows.  The four
+// waves' states merge in LDS (wave h merges head h); a piece that is a whole
+// segment stores the output, otherwise it publishes its partial and the last
+// piece to arrive merges the segment.
 template <int HD, int GM>
 __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lane) {
+  static_assert(GM <= 8, "at most 8 query heads per KV head");
   A = uni(A);
   char* ring = mk_lds;
-  // per-wave softmax states live in the GEMV staging buffer while attention runs
-  float* red = (float*)xb_stage(A);
   Ctrl* c = ctrl_block(A);
   CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
-  constexpr int LPR = HD / 8, RP = 64 / LPR, RPC = 4096 / HD;
+  constexpr int LPR = HD / 8, RP = 64 / LPR, RPC = 4096 / HD, NP = RPC / RP;
+  constexpr int NRB = RPC / 16;        // 16-row blocks per chunk (MFMA N)
+  constexpr int NDS = HD / 32;         // 32-wide steps over the head dimension (MFMA K)
+  constexpr int PH = GM <= 4 ? 4 : 8;  // heads per row of the probability buffer
+  constexpr int SW = HD + 4;           // floats per head in a state / partial record
   constexpr float kLog2e = 1.4426950408889634f;
   const int l = t.layer, G = A->G, e0 = (lane % LPR) * 8, gi = lane / LPR;
+  const int r16 = lane & 15, lr = lane >> 4;  // MFMA output layout: row r16 of a block, heads 4 lr + i
   const float qscale = kLog2e / sqrtf((float)HD);
   const long long W = attn_total(c, A->b, A->nkv);
   long long pos = cu_lo(cu, W, A->ncu), hi = cu_lo(cu + 1, W, A->ncu);
   Piece P;
   int qc = s.q, pidx = 0;
   const MK_AS4 LayerW& lw = as_const(A->layers)[l];
-  const int stride_st = kComputeWaves * GM * (HD + 4);
-  // trace: attention phase totals of compute wave 0 (per-CU stats words 32..40)
+  // staging-buffer layout while attention runs: wave states (2 piece
+  // parities x 4 waves x GM x SW), then per wave the scaled queries (GM x HD)
+  // and the chunk's probabilities (RPC x PH)
+  float* stb = (float*)xb_stage(A);
+  const int stride_st = kComputeWaves * GM * SW;
+  float* qb = stb + 2 * stride_st + w * GM * HD;
+  float* pb = stb + 2 * stride_st + kComputeWaves * GM * HD + w * RPC * PH;
+  // trace: attention phase totals of compute wave 0 (per-CU stats words 32..41)
   uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0)
                       ? A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32
                       : nullptr;
@@ -1260,26 +1282,52 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       tlast = tn;
     }
   };
+  auto bcast = [](float v, int src_lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
+  };
   while (next_piece(c, A->b, A->nkv, RPC, pos, hi, P)) {
     const int p = c->slen[P.i] - 1;
     if (ast) ast[7] += 1;
     const float* qrow = A->qkv + ((size_t)l * A->bcap + P.i) * A->nqkv;
-    float q[GM][8], o[GM][8];
-    SoftState st[GM];
+    // queries: QK-norm + RoPE + scale (each lane group holds dims e0..e0+7),
+    // then this wave's copy in LDS re-read in the MFMA A layout
+    float q[GM][8];
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
-      st[h].m = -INFINITY;
-      st[h].l = 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) o[h][u] = 0.f;
       if (h < G) {
         rope_head<HD>(A, qrow + (size_t)(P.g * G + h) * HD, A->qk_norm ? lw.q_norm : nullptr, p, e0, q[h]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) q[h][u] *= qscale;
+        if (gi == 0) {
+          lds_st16((char*)(qb + h * HD + e0), u32x4{__float_as_uint(q[h][0]), __float_as_uint(q[h][1]),
+                                                    __float_as_uint(q[h][2]), __float_as_uint(q[h][3])});
+          lds_st16((char*)(qb + h * HD + e0 + 4), u32x4{__float_as_uint(q[h][4]), __float_as_uint(q[h][5]),
+                                                        __float_as_uint(q[h][6]), __float_as_uint(q[h][7])});
+        }
       } else {
 #pragma unroll
         for (int u = 0; u < 8; ++u) q[h][u] = 0.f;
       }
+    }
+    u32x4 qa_hi[NDS], qa_lo[NDS];
+    {
+      const int kq = 8 * lr;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        qa_hi[ds] = qa_lo[ds] = u32x4{0, 0, 0, 0};
+        if (r16 < G) {
+          const char* src = (const char*)(qb + r16 * HD + ds * 32 + kq);
+          split8(lds_ld16(src), lds_ld16(src + 16), qa_hi[ds], qa_lo[ds]);
+        }
+      }
+    }
+    float mrun[GM], lrun[GM], o[GM][8];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      mrun[h] = -INFINITY;
+      lrun[h] = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[h][u] = 0.f;
     }
     mark(0);
     // cached rows, streamed by the loader
@@ -1291,64 +1339,90 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       if (MK_PHASE_TRACE && ast) ast[9] += now_ticks() - tw0;
       const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
       const int rows = min(RPC, P.ncached - ch * RPC);
-      // scores of every row of the chunk first (lane group gi holds rows
-      // gi, gi + RP, ...), then one online-softmax rescale per chunk
-      constexpr int NP = RPC / RP;  // passes per chunk
-      float sc[GM][NP];
+      // scores S[head][row]: lane holds heads 4 lr + i of row rb * 16 + r16
+      f32x4 S[NRB];
 #pragma unroll
-      for (int pass = 0; pass < NP; ++pass) {
-        const int row = pass * RP + gi;
-        float kf[8];
-        unpack8(lds_ld16(slot + row * HD * 2 + e0 * 2), kf);
+      for (int rb = 0; rb < NRB; ++rb) {
+        S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          float d = 0.f;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) d += q[h][u] * kf[u];
-          sc[h][pass] = d;
+        for (int ds = 0; ds < NDS; ++ds) {
+          const u32x4 kb = lds_ld16(slot + ((rb * 16 + r16) * HD + ds * 32 + 8 * lr) * 2);
+          S[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa_lo[ds]),
+                                                          __builtin_bit_cast(bf16x8_t, kb), S[rb], 0, 0, 0);
+          S[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa_hi[ds]),
+                                                          __builtin_bit_cast(bf16x8_t, kb), S[rb], 0, 0, 0);
         }
+      }
+      // chunk maxima per head (rows past the chunk's end are -inf)
+      float mx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          S[rb][i] = rb * 16 + r16 < rows ? S[rb][i] : -INFINITY;
+          m = fmaxf(m, S[rb][i]);
+        }
+        mx[i] = group_max<16>(m);
+      }
+      float mnew[GM], fa[GM];
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        mnew[h] = fmaxf(mrun[h], bcast(mx[h & 3], 16 * (h >> 2)));
+        fa[h] = mnew[h] == -INFINITY ? 1.f : exp2f(mrun[h] - mnew[h]);
+      }
+      // probabilities of this lane's rows for its heads, row sums, to LDS
+      float ls[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mh = (PH > 4 && lr == 1) ? mnew[(4 + i) % GM] : mnew[i % GM];
+        float sum = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float pv = S[rb][i] == -INFINITY ? 0.f : exp2f(S[rb][i] - mh);
+          S[rb][i] = pv;
+          sum += pv;
+        }
+        ls[i] = group_sum<16>(sum);
+      }
+      if (lr < PH / 4) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          lds_st16((char*)(pb + (rb * 16 + r16) * PH + 4 * lr),
+                   u32x4{__float_as_uint(S[rb][0]), __float_as_uint(S[rb][1]), __float_as_uint(S[rb][2]), __float_as_uint(S[rb][3])});
       }
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
-        if (h >= G) continue;
-        float mx = -INFINITY;
+        lrun[h] = lrun[h] * fa[h] + bcast(ls[h & 3], 16 * (h >> 2));
+        mrun[h] = mnew[h];
 #pragma unroll
-        for (int pass = 0; pass < NP; ++pass) {
-          // rows past the chunk's end get -inf added (the sum itself is
-          // always used, see dpp_f)
-          sc[h][pass] = group_sum<LPR>(sc[h][pass]) + (pass * RP + gi < rows ? 0.f : -INFINITY);
-          mx = fmaxf(mx, sc[h][pass]);
-        }
-        const float mn = fmaxf(st[h].m, mx);
-        const float fa = mn == -INFINITY ? 1.f : exp2f(st[h].m - mn);
-        float lsum = 0.f;
-#pragma unroll
-        for (int pass = 0; pass < NP; ++pass) {
-          const float pw = sc[h][pass] == -INFINITY ? 0.f : exp2f(sc[h][pass] - mn);
-          sc[h][pass] = pw;
-          lsum += pw;
-        }
-        st[h].l = st[h].l * fa + lsum;
-        st[h].m = mn;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[h][u] *= fa;
+        for (int u = 0; u < 8; ++u) o[h][u] *= fa[h];
       }
+      // V rows: lane group gi takes rows gi, gi + RP, ...
 #pragma unroll
       for (int pass = 0; pass < NP; ++pass) {
         const int row = pass * RP + gi;
-        float vf[8];
-        unpack8(lds_ld16(slot + 8192 + row * HD * 2 + e0 * 2), vf);
+        float vf[8], ph[PH];
+        unpack8(lds_ld16(slot + 8192 + (row * HD + e0) * 2), vf);
+#pragma unroll
+        for (int k = 0; k < PH / 4; ++k) {
+          const u32x4 pv = lds_ld16((const char*)(pb + row * PH + 4 * k));
+          ph[4 * k] = __uint_as_float(pv.x);
+          ph[4 * k + 1] = __uint_as_float(pv.y);
+          ph[4 * k + 2] = __uint_as_float(pv.z);
+          ph[4 * k + 3] = __uint_as_float(pv.w);
+        }
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
           if (h >= G) continue;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) o[h][u] += sc[h][pass] * vf[u];
+          for (int u = 0; u < 8; ++u) o[h][u] += ph[h] * vf[u];
         }
       }
       free_chunk(A, c, gq, lane);
     }
     // the new row: K after QK-norm + RoPE, V raw, both rounded to bf16,
-    // written to the cache and absorbed by lane group 0 of wave 0
+    // written to the cache and absorbed by wave 0 (lane group 0 adds V)
     if (w == 0 && P.has_new) {
       float kn[8], vn[8];
       const float* krow = qrow + A->qdim + (size_t)P.g * HD;
@@ -1372,45 +1446,38 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         float sc = 0.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) sc += q[h][u] * kn[u];
-        sc = group_sum<LPR>(sc);
-        if (gi == 0) {
-          const float mn = fmaxf(st[h].m, sc);
-          const float fa = exp2f(st[h].m - mn), pw = exp2f(sc - mn);
-          st[h].l = st[h].l * fa + pw;
+        sc = bcast(group_sum<LPR>(sc), 0);  // every lane group computed the same row
+        const float mn = fmaxf(mrun[h], sc);
+        const float fa = exp2f(mrun[h] - mn), pw = exp2f(sc - mn);
+        lrun[h] = lrun[h] * fa + pw;
+        mrun[h] = mn;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) o[h][u] = o[h][u] * fa + pw * vn[u];
-          st[h].m = mn;
-        }
+        for (int u = 0; u < 8; ++u) o[h][u] = o[h][u] * fa + (gi == 0 ? pw * vn[u] : 0.f);
       }
     }
     mark(1);
-    // merge the lane groups of this wave
+    // sum the lane groups (they share this wave's m), then wave state -> LDS
 #pragma unroll
     for (int msk = LPR; msk < 64; msk <<= 1) {
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h >= G) continue;
-        const float m2 = __shfl_xor(st[h].m, msk), l2 = __shfl_xor(st[h].l, msk);
-        const float mn = fmaxf(st[h].m, m2);
-        const float fa = mn == -INFINITY ? 0.f : exp2f(st[h].m - mn);
-        const float fb = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o[h][u] = o[h][u] * fa + __shfl_xor(o[h][u], msk) * fb;
-        st[h].l = st[h].l * fa + l2 * fb;
-        st[h].m = mn;
+        for (int u = 0; u < 8; ++u) o[h][u] += __shfl_xor(o[h][u], msk);
       }
     }
-    // wave states -> LDS (double-buffered by piece parity)
-    float* sb = red + (pidx & 1) * stride_st + w * GM * (HD + 4);
+    float* sb = stb + (pidx & 1) * stride_st + w * GM * SW;
     if (gi == 0) {
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h >= G) continue;
-        *(f32x4*)(sb + h * (HD + 4) + e0) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
-        *(f32x4*)(sb + h * (HD + 4) + e0 + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+        lds_st16((char*)(sb + h * SW + e0), u32x4{__float_as_uint(o[h][0]), __float_as_uint(o[h][1]),
+                                                  __float_as_uint(o[h][2]), __float_as_uint(o[h][3])});
+        lds_st16((char*)(sb + h * SW + e0 + 4), u32x4{__float_as_uint(o[h][4]), __float_as_uint(o[h][5]),
+                                                      __float_as_uint(o[h][6]), __float_as_uint(o[h][7])});
         if (lane == 0) {
-          sb[h * (HD + 4) + HD] = st[h].m;
-          sb[h * (HD + 4) + HD + 1] = st[h].l;
+          sb[h * SW + HD] = mrun[h];
+          sb[h * SW + HD + 1] = lrun[h];
         }
       }
     }
@@ -1421,125 +1488,108 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     // CUs whose range is empty (fewer rows than CUs) hold no piece
     const int npieces = W >= A->ncu ? c_last - c_first + 1
                                    : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
-    const int pstride = GM * (HD + 4);
+    const int pstride = GM * SW;
     float* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
-    if (w == 0) {
-      // merge the 4 wave states (lane group 0 holds 8 elements per lane)
-      const float* s0 = red + (pidx & 1) * stride_st;
-      float M[GM], Lsum[GM], O[GM][8];
+    float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
+    // merge the four wave states: wave w takes heads w, w + 4; each lane HD/64 dims
+    constexpr int DPL = HD / 64;
+    const float* s0 = stb + (pidx & 1) * stride_st;
+    for (int h = w; h < G; h += kComputeWaves) {
+      float M = -INFINITY, L = 0.f, O[DPL];
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        M[h] = -INFINITY;
-        Lsum[h] = 0.f;
+      for (int k = 0; k < DPL; ++k) O[k] = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) O[h][u] = 0.f;
-        if (h >= G) continue;
-        for (int ww = 0; ww < kComputeWaves; ++ww) {
-          const float* e = s0 + ww * GM * (HD + 4) + h * (HD + 4);
-          const float m2 = e[HD], l2 = e[HD + 1];
-          const float mn = fmaxf(M[h], m2);
-          const float fa = mn == -INFINITY ? 0.f : exp2f(M[h] - mn);
-          const float fb = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
+      for (int ww = 0; ww < kComputeWaves; ++ww) {
+        const float* e = s0 + ww * GM * SW + h * SW;
+        const float m2 = e[HD], l2 = e[HD + 1];
+        const float mn = fmaxf(M, m2);
+        const float fa = mn == -INFINITY ? 0.f : exp2f(M - mn);
+        const float fb = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) O[h][u] = O[h][u] * fa + e[e0 + u] * fb;
-          Lsum[h] = Lsum[h] * fa + l2 * fb;
-          M[h] = mn;
-        }
+        for (int k = 0; k < DPL; ++k) O[k] = O[k] * fa + e[DPL * lane + k] * fb;
+        L = L * fa + l2 * fb;
+        M = mn;
       }
-      int fin = 0;
       if (npieces == 1) {
         // the whole segment is here: normalise and store
-        if (gi == 0) {
-#pragma unroll
-          for (int h = 0; h < GM; ++h) {
-            if (h >= G) continue;
-            const float inv = 1.0f / Lsum[h];
-            co_store16(ob, (uint32_t)((h * HD + e0) * 4),
-                       u32x4{__float_as_uint(O[h][0] * inv), __float_as_uint(O[h][1] * inv),
-                             __float_as_uint(O[h][2] * inv), __float_as_uint(O[h][3] * inv)});
-            co_store16(ob, (uint32_t)((h * HD + e0 + 4) * 4),
-                       u32x4{__float_as_uint(O[h][4] * inv), __float_as_uint(O[h][5] * inv),
-                             __float_as_uint(O[h][6] * inv), __float_as_uint(O[h][7] * inv)});
-          }
-        }
+        const float inv = 1.0f / L;
+        if constexpr (DPL == 2) co_store8(ob, (uint32_t)((h * HD + 2 * lane) * 4), u32x2{__float_as_uint(O[0] * inv), __float_as_uint(O[1] * inv)});
+        else co_storef(ob, (uint32_t)((h * HD + lane) * 4), O[0] * inv);
       } else {
-        // publish this piece; the last piece of the segment to arrive merges
-        float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
-        if (gi == 0) {
-#pragma unroll
-          for (int h = 0; h < GM; ++h) {
-            if (h >= G) continue;
-            co_store16(dst, (uint32_t)((h * (HD + 4) + e0) * 4),
-                       u32x4{__float_as_uint(O[h][0]), __float_as_uint(O[h][1]), __float_as_uint(O[h][2]), __float_as_uint(O[h][3])});
-            co_store16(dst, (uint32_t)((h * (HD + 4) + e0 + 4) * 4),
-                       u32x4{__float_as_uint(O[h][4]), __float_as_uint(O[h][5]), __float_as_uint(O[h][6]), __float_as_uint(O[h][7])});
-            if (lane == 0) co_store8(dst, (uint32_t)((h * (HD + 4) + HD) * 4), u32x2{__float_as_uint(M[h]), __float_as_uint(Lsum[h])});
-          }
-        }
-        wait_mem();
+        if constexpr (DPL == 2) co_store8(dst, (uint32_t)((h * SW + 2 * lane) * 4), u32x2{__float_as_uint(O[0]), __float_as_uint(O[1])});
+        else co_storef(dst, (uint32_t)((h * SW + lane) * 4), O[0]);
+        if (lane == 0) co_store8(dst, (uint32_t)((h * SW + HD) * 4), u32x2{__float_as_uint(M), __float_as_uint(L)});
+      }
+    }
+    mark(3);
+    if (npieces > 1) {
+      // the last piece of the segment to arrive merges it
+      wait_mem();
+      if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+      if (w == 0) {
         uint32_t old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(A->seg_ctr + P.sid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
-        fin = (int)old == npieces - 1;
+        const int fin = (int)old == npieces - 1;
         if (fin && lane == 0) __hip_atomic_store(A->seg_ctr + P.sid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) lds_st_rel(&c->fin, fin);
       }
-      if (lane == 0) lds_st_rel(&c->fin, fin);
-      mark(3);
-    }
-    if (npieces > 1) {
       if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
       if (lds_ld_acq(&c->fin)) {
-        // merge every piece of the segment: compute wave w takes heads
-        // w, w + 4; LPP lanes cover one piece's head vector, 64 / LPP pieces
-        // per pass, all loads of kMergeUnroll passes issued together
-        constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeUnroll = 8;
+        // compute wave w merges heads w, w + 4: LPP lanes cover one piece's
+        // head vector, PPI pieces per pass; all loads of a batch are issued
+        // before any is used
+        constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeIt = 16;
         const int sub = lane / LPP, el = (lane % LPP) * 4;
         auto piece_src = [&](int pc) -> const float* {
           const int pcu = W >= A->ncu ? c_first + pc : cu_of(P.seg_start + pc, W, A->ncu);
           return A->apart + (size_t)(pcu + P.sid) * pstride;
         };
         for (int h = w; h < G; h += kComputeWaves) {
-          // maximum over the pieces' running maxima
-          float mv = -INFINITY;
-          for (int p0 = 0; p0 < npieces; p0 += 64) {
-            const int pc = p0 + lane;
-            if (pc < npieces) mv = fmaxf(mv, co_loadf(piece_src(pc), (uint32_t)((h * (HD + 4) + HD) * 4)));
-          }
-          mv = group_max<16>(mv);
-          mv = fmaxf(mv, __shfl_xor(mv, 16));
-          mv = fmaxf(mv, __shfl_xor(mv, 32));
+          float Mrun = -INFINITY, Lrun = 0.f;
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          float lsum = 0.f;
-          for (int p0 = 0; p0 < npieces; p0 += PPI * kMergeUnroll) {
-            u32x4 ov[kMergeUnroll];
-            float m2[kMergeUnroll], l2[kMergeUnroll];
+          for (int p0 = 0; p0 < npieces; p0 += PPI * kMergeIt) {
+            u32x4 ov[kMergeIt];
+            float m2[kMergeIt], l2[kMergeIt];
 #pragma unroll
-            for (int k = 0; k < kMergeUnroll; ++k) {
+            for (int k = 0; k < kMergeIt; ++k) {
               const int pc = p0 + k * PPI + sub;
               const float* src = piece_src(pc < npieces ? pc : 0);
-              ov[k] = co_load16(src, (uint32_t)((h * (HD + 4) + el) * 4));
-              m2[k] = co_loadf(src, (uint32_t)((h * (HD + 4) + HD) * 4));
-              l2[k] = co_loadf(src, (uint32_t)((h * (HD + 4) + HD + 1) * 4));
+              ov[k] = co_load16(src, (uint32_t)((h * SW + el) * 4));
+              const u32x2 ml = co_load8(src, (uint32_t)((h * SW + HD) * 4));
+              m2[k] = pc < npieces ? __uint_as_float(ml.x) : -INFINITY;
+              l2[k] = __uint_as_float(ml.y);
             }
+            float mb = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < kMergeUnroll; ++k) {
-              const int pc = p0 + k * PPI + sub;
-              const float f = (pc < npieces && m2[k] != -INFINITY) ? exp2f(m2[k] - mv) : 0.f;
+            for (int k = 0; k < kMergeIt; ++k) mb = fmaxf(mb, m2[k]);
+            mb = group_max<16>(mb);
+            mb = fmaxf(mb, __shfl_xor(mb, 16));
+            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            const float mn = fmaxf(Mrun, mb);
+            const float fr = Mrun == -INFINITY ? 0.f : exp2f(Mrun - mn);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] *= fr;
+            Lrun *= fr;
+#pragma unroll
+            for (int k = 0; k < kMergeIt; ++k) {
+              const float f = m2[k] == -INFINITY ? 0.f : exp2f(m2[k] - mn);
               acc[0] += f * __uint_as_float(ov[k].x);
               acc[1] += f * __uint_as_float(ov[k].y);
               acc[2] += f * __uint_as_float(ov[k].z);
               acc[3] += f * __uint_as_float(ov[k].w);
-              lsum += f * l2[k];
+              Lrun += f * l2[k];
             }
+            Mrun = mn;
           }
 #pragma unroll
           for (int msk = LPP; msk < 64; msk <<= 1) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[u] += __shfl_xor(acc[u], msk);
-            lsum += __shfl_xor(lsum, msk);
+            Lrun += __shfl_xor(Lrun, msk);
           }
           if (sub == 0) {
-            const float inv = 1.0f / lsum;
+            const float inv = 1.0f / Lrun;
             co_store16(ob, (uint32_t)((h * HD + el) * 4),
                        u32x4{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
                              __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)});
