@@ -15,7 +15,7 @@ namespace mk {
 // loader waves stream weights and cached K/V rows into an LDS ring and never
 // wait on a dependency counter.
 constexpr int kComputeWaves = 4;
-constexpr int kLoaderWaves = 4;
+constexpr int kLoaderWaves = 3;
 constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
 constexpr int kComputeThreads = 64 * kComputeWaves;
 constexpr int kChunkBytes = 16384;          // one LDS ring slot

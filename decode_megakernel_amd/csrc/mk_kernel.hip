@@ -2,7 +2,7 @@
 //
 // One work-group per CU walks that CU's instruction stream (built on the host,
 // see mk_plan.cpp).  Inside a work-group:
-//   * 4 loader waves stream every input-independent byte the CU's tasks need
+//   * 3 loader waves stream every input-independent byte the CU's tasks need
 //     (weight tiles, cached K/V rows) from HBM into an LDS ring with
 //     non-temporal loads.  They never wait on a dependency counter, so weights
 //     for later tasks arrive while the CU is still waiting for activations

@@ -143,7 +143,7 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
  * least (n_cu*cap*4 + n_cu*64)*8 bytes): for each CU and each of its first
  * `cap` tasks, 4 uint64 words {task index << 32 | layer << 16 | type << 8 | stage,
  * begin, dependency satisfied, end} in s_memrealtime ticks (100 MHz); then
- * 64 uint64 per CU: [0..3] ticks the loader waves waited for a free LDS
+ * 64 uint64 per CU: [0..2] ticks the loader waves waited for a free LDS
  * slot, [4..7] the compute waves waited for a loaded chunk, [8..11] the
  * compute waves waited in barriers, [12] compute wave 0's total time, [13]
  * loader wave 0's total time, [16..19] compute chunk math, [20..23] GEMV
