@@ -40,7 +40,10 @@ constexpr int kAttnStateBytes =
         ? (2 * 4 * 8 * (64 + 4) + 4 * 8 * 64 + 4 * 64 * 8) * 4
         : (2 * 4 * 4 * (128 + 4) + 4 * 4 * 128 + 4 * 32 * 4) * 4;
 constexpr int kStatWords = 64;               // trace: per-CU phase totals (uint64 words)
-constexpr int kCtrlBytes = 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
+#ifndef MK_PHASE_TRACE
+#define MK_PHASE_TRACE 0
+#endif
+constexpr int kCtrlBytes = MK_PHASE_TRACE ? 1536 : 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
 constexpr int kApartGroup = 8;               // group slots per attention partial
 
 enum Stage : int32_t { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_LM = 5, ST_EMBED = 6 };

@@ -19,13 +19,12 @@
 
 #include "mk_internal.h"
 
+#include <utility>
+
 // Per-phase timers of the in-kernel trace (per-CU stats words 32..61).  They
 // cost registers in the task functions, so they are compiled only into
 // analysis builds (-DMK_PHASE_TRACE=1); the per-task timestamps and the
 // wait totals are always available.
-#ifndef MK_PHASE_TRACE
-#define MK_PHASE_TRACE 0
-#endif
 
 namespace mk {
 
@@ -194,6 +193,9 @@ struct Ctrl {
   int slen[kMaxBatch];
   int tok[kMaxBatch];
   float rms[kMaxBatch];
+#if MK_PHASE_TRACE
+  uint64_t pstat[32];  // phase timers of compute wave 0, flushed at the end
+#endif
 };
 
 static_assert(sizeof(Ctrl) <= kCtrlBytes, "control block exceeds its LDS budget");
@@ -244,6 +246,27 @@ __device__ __forceinline__ bool spin_ok(DArgs A, Ctrl* c, Spin& sp) {
   }
   __builtin_amdgcn_s_sleep(1);
   return true;
+}
+
+// Phase-trace accumulation into the control block (LDS): no global memory
+// operation, so the timers add no wait to the phases they time.
+__device__ __forceinline__ void trace_add(uint64_t* p, uint64_t v) { *p += v; }
+#if MK_PHASE_TRACE
+#define MK_PSTAT(c, k) ((c)->pstat + (k))
+#else
+#define MK_PSTAT(c, k) ((uint64_t*)nullptr)
+#endif
+
+// f(integral_constant<int, 0>), f(..1), ... while f returns true: a loop
+// over per-tile register arrays whose index must be a compile-time constant
+// (a runtime index puts the array in scratch memory).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (void)(f(std::integral_constant<int, I>{}) && ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Software barrier among the compute waves (the loader waves never join).
@@ -795,20 +818,54 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   const int per_row = ksl / 8;
   const int units = A->b * per_row;
   const int tid = w * 64 + lane;
-  for (int u = tid; u < units; u += kComputeThreads) {
-    int n = u / per_row, kq = u - n * per_row;
-    const uint32_t off = (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 4);
-    u32x4 hi, lo;
-    split8(co_load16(x, off), co_load16(x, off + 16), hi, lo);
-    lds_st16(xb + ((size_t)n * ksp + 8 * kq) * 2, hi);
-    lds_st16(xlo + ((size_t)n * ksp + 8 * kq) * 2, lo);
-  }
+  // RMS partial sums of sequence w, loaded together with the input slice
   const float* ss = stage_ss(A, t.stage, t.layer);
-  if (ss && !(s.r_stage == t.stage && s.r_layer == t.layer)) {
-    const int nt = A->d / 16;
+  const bool rms = ss && !(s.r_stage == t.stage && s.r_layer == t.layer);
+  const int nt = A->d / 16;
+  constexpr int kSsLoads = 8;  // d / 16 / 64 partials per lane (hidden <= 8192)
+  float ssv[kSsLoads];
+#pragma unroll
+  for (int k = 0; k < kSsLoads; ++k) {
+    const int i = lane + 64 * k;
+    ssv[k] = (rms && w < A->b && i < nt) ? co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + w) * 4)) : 0.f;
+  }
+  // up to kStageBatch units per thread in flight at once: one memory round
+  // trip per batch rather than per unit
+  constexpr int kStageBatch = 4;
+  for (int u0 = tid; u0 < units; u0 += kStageBatch * kComputeThreads) {
+    u32x4 va[kStageBatch], vb[kStageBatch];
+#pragma unroll
+    for (int k = 0; k < kStageBatch; ++k) {
+      const int u = u0 + k * kComputeThreads;
+      const int n = u / per_row, kq = u - n * per_row;
+      const uint32_t off = (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 4);
+      va[k] = vb[k] = u32x4{0, 0, 0, 0};
+      if (u < units) {
+        va[k] = co_load16(x, off);
+        vb[k] = co_load16(x, off + 16);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kStageBatch; ++k) {
+      const int u = u0 + k * kComputeThreads;
+      const int n = u / per_row, kq = u - n * per_row;
+      if (u < units) {
+        u32x4 hi, lo;
+        split8(va[k], vb[k], hi, lo);
+        lds_st16(xb + ((size_t)n * ksp + 8 * kq) * 2, hi);
+        lds_st16(xlo + ((size_t)n * ksp + 8 * kq) * 2, lo);
+      }
+    }
+  }
+  if (rms) {
     for (int n = w; n < A->b; n += kComputeWaves) {
       float acc = 0.f;
-      for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4));
+      if (n == w) {
+#pragma unroll
+        for (int k = 0; k < kSsLoads; ++k) acc += ssv[k];
+      } else {
+        for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4));
+      }
       acc = group_sum<16>(acc);
       acc += __shfl_xor(acc, 16);
       acc += __shfl_xor(acc, 32);
@@ -893,19 +950,44 @@ __device__ __forceinline__ void valu_reduce(float (&acc)[16][NB], int lane, floa
 //      k-step into the same accumulator.
 __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int xlo_off, int ksp, int kl, int klen, int b,
                                            int lane, f32x4& acc) {
-  const int n = lane & 15, kq = 8 * (lane >> 4);
+  // columns n >= b of the B operand repeat column b - 1: their outputs are
+  // never stored, and every LDS read stays inside the staged rows
+  const int n = min(lane & 15, b - 1), kq = 8 * (lane >> 4);
+  const char* xh = xb + ((size_t)n * ksp + kl + kq) * 2;
+  const char* xl = xh + xlo_off;
+  const char* wv = slot + lane * 16;
+  f32x4 alo = {0.f, 0.f, 0.f, 0.f};  // the lo halves accumulate separately (two independent MFMA chains)
+  if (kl + kKBlock <= klen) {
+    // whole 512-wide block: LDS reads four K-steps at a time ahead of their MFMAs
 #pragma unroll
-  for (int s = 0; s < kWaveLoads; ++s) {
-    if (kl + 32 * s >= klen) break;
-    const int k = kl + 32 * s + kq;
-    u32x4 bh = n < b ? lds_ld16(xb + ((size_t)n * ksp + k) * 2) : u32x4{0, 0, 0, 0};
-    u32x4 bl = n < b ? lds_ld16(xb + xlo_off + ((size_t)n * ksp + k) * 2) : u32x4{0, 0, 0, 0};
-    u32x4 av = lds_ld16(slot + s * 1024 + lane * 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bl),
-                                                  acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bh),
-                                                  acc, 0, 0, 0);
+    for (int s0 = 0; s0 < kWaveLoads; s0 += 4) {
+      u32x4 bh[4], bl[4], av[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        av[u] = lds_ld16(wv + (s0 + u) * 1024);
+        bh[u] = lds_ld16(xh + (s0 + u) * 64);
+        bl[u] = lds_ld16(xl + (s0 + u) * 64);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        alo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]), __builtin_bit_cast(bf16x8_t, bl[u]),
+                                                      alo, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]), __builtin_bit_cast(bf16x8_t, bh[u]),
+                                                      acc, 0, 0, 0);
+      }
+    }
+  } else {
+    // the ragged last block of K: steps of 32 up to klen (klen - kl is a multiple of 32)
+    for (int s = 0; s < kWaveLoads && kl + 32 * s < klen; ++s) {
+      const u32x4 av = lds_ld16(wv + s * 1024), bh = lds_ld16(xh + s * 64), bl = lds_ld16(xl + s * 64);
+      alo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bl), alo,
+                                                    0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bh), acc,
+                                                    0, 0, 0);
+    }
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] += alo[q];
 }
 
 // Epilogue of one output element (row `lr` of the stage, sequence n) of a
@@ -913,7 +995,7 @@ __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int
 // group holds one sequence's 16 consecutive rows.  `resid` is the residual
 // prefetched for O / DOWN.
 __device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, int lr, int row, int n, float val, float val_up,
-                              float resid, int lane) {
+                              float resid, float nw, int lane) {
   const int l = t.layer;
   const int M = stage_M(A, t.stage);
   const bool valid = n < A->b && lr < M;
@@ -928,11 +1010,10 @@ __device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, i
       const bool down = t.stage == ST_DOWN;
       float* hout = down ? A->hres + (size_t)(l + 1) * A->bcap * A->d : A->hmid + (size_t)l * A->bcap * A->d;
       float* xo = down ? A->xattn + (size_t)(l + 1) * A->bcap * A->d : A->xmlp + (size_t)l * A->bcap * A->d;
-      const uint16_t* nw = down ? (l + 1 < A->L ? as_const(A->layers)[l + 1].attn_norm : A->final_norm) : as_const(A->layers)[l].mlp_norm;
       float* ssout = down ? A->ssattn + (size_t)(l + 1) * (A->d / 16) * A->bcap : A->ssmlp + (size_t)l * (A->d / 16) * A->bcap;
       const uint32_t off = (uint32_t)(((size_t)n * A->d + lr) * 4);
       float h = valid ? resid + val : 0.f;
-      const float xn = valid ? h * bf2f(nw[lr]) : 0.f;
+      const float xn = valid ? h * nw : 0.f;
       if (valid) {
         co_storef(hout, off, h);
         co_storef(xo, off, xn);
@@ -990,33 +1071,48 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
   const int nsub = t.nsub;
-  const int nown = nsub > w ? min(TPW, (nsub - w + kComputeWaves - 1) / kComputeWaves) : 0;
+  // Fewer sub-tiles than compute waves: the waves of one sub-tile split its
+  // K blocks (wave w takes sub-tile w % nsub, blocks kb = w / nsub mod S) and
+  // sum their partial tiles in LDS before the epilogue.
+  const int S = nsub == 1 ? kComputeWaves : (nsub == 2 ? kComputeWaves / 2 : 1);
+  const int kpart = S > 1 ? w / nsub : 0;
+  const int msub = S > 1 ? w % nsub : w;  // this wave's (first) sub-tile
+  const int nown = S > 1 ? 1 : (nsub > w ? min(TPW, (nsub - w + kComputeWaves - 1) / kComputeWaves) : 0);
   const int M = stage_M(A, t.stage);
   const int nkb = (t.k1 - t.k0 + kKBlock - 1) / kKBlock;
   const int row = lane & 15;
   const bool has_resid = t.stage == ST_O || t.stage == ST_DOWN;
   const float* hin = t.stage == ST_DOWN ? A->hmid + (size_t)t.layer * A->bcap * A->d
                                         : A->hres + (size_t)t.layer * A->bcap * A->d;
-  // residuals of the first owned rows, prefetched while the weights stream
-  float resid[kResidTiles][4];
+  auto tile_row0 = [&](int i) { return t.row0 + 16 * (msub + kComputeWaves * i); };
+  // residuals and next-norm weights of the first owned rows, prefetched
+  // while the weights stream (only the wave that runs the epilogue needs them)
+  const bool lead = kpart == 0;
+  const uint16_t* nwp = nullptr;
+  if (t.stage == ST_O) nwp = as_const(A->layers)[t.layer].mlp_norm;
+  if (t.stage == ST_DOWN) nwp = t.layer + 1 < A->L ? as_const(A->layers)[t.layer + 1].attn_norm : A->final_norm;
+  float resid[kResidTiles][4], nwv[kResidTiles];
 #pragma unroll
-  for (int i = 0; i < kResidTiles; ++i)
+  for (int i = 0; i < kResidTiles; ++i) {
+    const int lr = tile_row0(i) + row;
+    nwv[i] = (has_resid && lead && i < nown && lr < M) ? bf2f(nwp[lr]) : 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       resid[i][j] = 0.f;
-      const int n = (lane >> 4) + 4 * j, lr = t.row0 + 16 * (w + kComputeWaves * i) + row;
-      if (has_resid && i < nown && n < A->b && lr < M) resid[i][j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4));
+      const int n = (lane >> 4) + 4 * j;
+      if (has_resid && lead && i < nown && n < A->b && lr < M) resid[i][j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4));
     }
+  }
   // trace: GEMV phase totals of compute wave 0, per stage (per-CU stats words
   // 42 + 4 * stage + {0 staging, 1 chunks, 2 reduce + epilogue, 3 signal})
   uint64_t* gst = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0)
-                      ? A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 42 + 4 * (t.stage == ST_LM ? 1 : t.stage)
+                      ? MK_PSTAT(c, 10 + 4 * (t.stage == ST_LM ? 1 : t.stage))
                       : nullptr;
   uint64_t gt = gst ? now_ticks() : 0;
   auto gmark = [&](int k) {
     if (gst) {
       const uint64_t tn = now_ticks();
-      gst[k] += tn - gt;
+      trace_add(gst + k, tn - gt);
       gt = tn;
     }
   };
@@ -1042,24 +1138,54 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     if (A->trace) s.t_stage += now_ticks() - ts0;
     gmark(0);
     const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0, xlo_off = A->b * ksp * 2;
-    for (int kb = wb; kb < we && nown > 0; ++kb) {
+    // first block of this window that belongs to this wave's K part
+    const int kb0 = S > 1 ? wb + ((kpart - wb) % S + S) % S : wb;
+    for (int kb = kb0; kb < we && nown > 0; kb += S) {
       const int kl = (kb - wb) * kKBlock;
+      if constexpr (NB > 0) {
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        if (i >= nown) break;
-        const int gq = s.q + kb * nsub + w + kComputeWaves * i;
-        if (!wait_chunk(A, c, gq, s.w_empty)) return false;
-        const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
-        const uint64_t tm0 = A->trace ? now_ticks() : 0;
-        if constexpr (NB > 0) valu_chunk<NB>(slot, xb, xlo_off, ksp, kl + 8 * lane, klen, lane, vacc[i]);
-        else mfma_chunk(slot, xb, xlo_off, ksp, kl, klen, A->b, lane, macc[i]);
-        free_chunk(A, c, gq, lane);
-        if (A->trace) s.t_math += now_ticks() - tm0;
+        for (int i = 0; i < TPW; ++i) {
+          if (i >= nown) break;
+          const int gq = s.q + kb * nsub + msub + kComputeWaves * i;
+          if (!wait_chunk(A, c, gq, s.w_empty)) return false;
+          const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
+          const uint64_t tm0 = A->trace ? now_ticks() : 0;
+          valu_chunk<NB>(slot, xb, xlo_off, ksp, kl + 8 * lane, klen, lane, vacc[i]);
+          free_chunk(A, c, gq, lane);
+          if (A->trace) s.t_math += now_ticks() - tm0;
+        }
+      } else {
+        // eight MFMA tiles per wave: a plain unrolled loop with an early exit
+        // is not always unrolled, and a runtime index would move the
+        // accumulators to scratch memory
+        bool ok = true;
+        static_for<TPW>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          if (i >= nown) return false;
+          const int gq = s.q + kb * nsub + msub + kComputeWaves * i;
+          if (!wait_chunk(A, c, gq, s.w_empty)) return ok = false;
+          const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
+          const uint64_t tm0 = A->trace ? now_ticks() : 0;
+          mfma_chunk(slot, xb, xlo_off, ksp, kl, klen, A->b, lane, macc[i]);
+          free_chunk(A, c, gq, lane);
+          if (A->trace) s.t_math += now_ticks() - tm0;
+          return true;
+        });
+        if (!ok) return false;
       }
     }
   }
   const uint64_t te0 = A->trace ? now_ticks() : 0;
   gmark(1);
+  // Land the prefetched residuals and norm weights now, while no store is in
+  // flight: a first use after the epilogue's stores would make the wait on
+  // them also wait for those stores.
+#pragma unroll
+  for (int i = 0; i < kResidTiles; ++i) {
+    asm volatile("" ::"v"(nwv[i]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(resid[i][j]));
+  }
   // owned sub-tile i's totals -> this wave's LDS scratch as [16 rows][16 n],
   // read back with lanes mapped to (row = lane & 15, n = lane / 16 + 4 j)
   float* rw = red + w * 256;
@@ -1083,11 +1209,42 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       up[j] = (t.stage == ST_GU && row < 8) ? rw[(row + 8) * 16 + n] : 0.f;
     }
   };
+  // K split inside the CU: every wave leaves its partial tile in its LDS
+  // scratch (tile_values), then the leading wave of each sub-tile adds the
+  // others' in a fixed order
+  float sval[4] = {0.f, 0.f, 0.f, 0.f}, sup[4] = {0.f, 0.f, 0.f, 0.f};
+  if (S > 1) {
+    tile_values(0, sval, sup);
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    if (lead) {
+      for (int k = 1; k < S; ++k) {
+        const float* ro = red + (w + nsub * k) * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = (lane >> 4) + 4 * j;
+          sval[j] += ro[row * 16 + n];
+          if (t.stage == ST_GU && row < 8) sup[j] += ro[(row + 8) * 16 + n];
+        }
+      }
+    }
+  }
+  auto owned_values = [&](int i, float (&val)[4], float (&up)[4]) {
+    if (S > 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        val[j] = sval[j];
+        up[j] = sup[j];
+      }
+    } else {
+      tile_values(i, val, up);
+    }
+  };
+  const int nepi = lead ? nown : 0;  // owned sub-tiles whose epilogue this wave runs
   if (t.nks > 1) {
-    // split K: one sub-tile per wave (nsub <= 4)
-    const bool own = nown > 0;
+    // split K: one sub-tile per leading wave (nsub <= 4)
+    const bool own = nepi > 0;
     float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
-    if (own) tile_values(0, val, up);
+    if (own) owned_values(0, val, up);
     float* pb = A->part + (size_t)(t.part_slot + t.ks) * 1024 + w * 256;
     if (own) {
 #pragma unroll
@@ -1117,29 +1274,39 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
         val[j] = v;
         up[j] = u;
       }
-      const int lr0 = t.row0 + 16 * w;
+      const int lr0 = tile_row0(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], lane);
+      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], nwv[0], lane);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      if (i >= nown) break;
+      if (i >= nepi) break;
       float val[4], up[4];
-      tile_values(i, val, up);
-      const int lr0 = t.row0 + 16 * (w + kComputeWaves * i);
+      if constexpr (NB > 0) {
+        owned_values(i, val, up);
+      } else {
+        // the accumulator array is indexed by constants only
+        static_for<TPW>([&](auto I) {
+          if (decltype(I)::value == i) owned_values(decltype(I)::value, val, up);
+          return true;
+        });
+      }
+      const int lr0 = tile_row0(i);
+      static_assert(kResidTiles == 2, "prefetched tiles are selected by constant index");
+      const float nw = i == 0 ? nwv[0] : (i == 1 ? nwv[1] : ((has_resid && lr0 + row < M) ? bf2f(nwp[lr0 + row]) : 0.f));
       float rs[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (i < kResidTiles) {
-          rs[j] = resid[i < kResidTiles ? i : 0][j];
+          rs[j] = i == 0 ? resid[0][j] : resid[1][j];
         } else {
           const int n = (lane >> 4) + 4 * j;
           rs[j] = (has_resid && n < A->b && lr0 + row < M) ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4)) : 0.f;
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], lane);
+      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], nw, lane);
     }
   }
   gmark(2);
@@ -1271,14 +1438,12 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   float* qb = stb + 2 * stride_st + w * GM * HD;
   float* pb = stb + 2 * stride_st + kComputeWaves * GM * HD + w * RPC * PH;
   // trace: attention phase totals of compute wave 0 (per-CU stats words 32..41)
-  uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0)
-                      ? A->trace + (size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32
-                      : nullptr;
+  uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0) ? MK_PSTAT(c, 0) : nullptr;
   uint64_t tlast = ast ? now_ticks() : 0;
   auto mark = [&](int k) {
     if (ast) {
       const uint64_t tn = now_ticks();
-      ast[k] += tn - tlast;
+      trace_add(ast + k, tn - tlast);
       tlast = tn;
     }
   };
@@ -1287,7 +1452,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   };
   while (next_piece(c, A->b, A->nkv, RPC, pos, hi, P)) {
     const int p = c->slen[P.i] - 1;
-    if (ast) ast[7] += 1;
+    if (ast) trace_add(ast + 7, 1);
     const float* qrow = A->qkv + ((size_t)l * A->bcap + P.i) * A->nqkv;
     // queries: QK-norm + RoPE + scale (each lane group holds dims e0..e0+7),
     // then this wave's copy in LDS re-read in the MFMA A layout
@@ -1336,7 +1501,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       if ((gq & (kComputeWaves - 1)) != w) continue;
       const uint64_t tw0 = MK_PHASE_TRACE && ast ? now_ticks() : 0;
       if (!wait_chunk(A, c, gq, s.w_empty)) return false;
-      if (MK_PHASE_TRACE && ast) ast[9] += now_ticks() - tw0;
+      if (MK_PHASE_TRACE && ast) trace_add(ast + 9, now_ticks() - tw0);
       const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
       const int rows = min(RPC, P.ncached - ch * RPC);
       // scores S[head][row]: lane holds heads 4 lr + i of row rb * 16 + r16
@@ -1596,7 +1761,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
           }
         }
         mark(4);
-        if (ast) ast[8] += 1;
+        if (ast) trace_add(ast + 8, 1);
       }
     }
     mark(5);
@@ -1691,6 +1856,10 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
     st[20 + w] = s.t_stage;
     st[24 + w] = s.t_epi;
     if (w == 0) st[12] = now_ticks() - t_kernel0;
+#if MK_PHASE_TRACE
+    if (w == 0)
+      for (int k = 0; k < 32; ++k) st[32 + k] = c->pstat[k];
+#endif
   }
   // Greedy tokens: once every LM task has signalled, the argmax keys are
   // final.  Every CU that ran LM tasks checks once; the CU whose signal was
@@ -1726,7 +1895,9 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
     c->freed[tid] = 0;
   }
   if (tid < kMaxBatch) c->lmkey[tid] = 0ull;
-  if (A->trace && tid < 32) A->trace[(size_t)A->ncu * A->trace_cap * 4 + (size_t)cu * kStatWords + 32 + tid] = 0;
+#if MK_PHASE_TRACE
+  if (tid < 32) c->pstat[tid] = 0;
+#endif
   if (tid == 0) {
     c->dep = 0;
     c->bar = 0;
