@@ -1263,16 +1263,32 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     const bool fin = lds_ld_acq(&c->fin) != 0;
     if (own && fin) {
       const float* p0 = A->part + (size_t)t.part_slot * 1024 + w * 256;
+      // sum the pieces in piece order, kSumBatch pieces' loads in flight at once
+      constexpr int kSumBatch = 8;
+      const bool gu_up = t.stage == ST_GU && row < 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = ((lane >> 4) + 4 * j) * 16 + row;
-        float v = 0.f, u = 0.f;
-        for (int k = 0; k < t.nks; ++k) {
-          v += co_loadf(p0, (uint32_t)(((size_t)k * 1024 + e) * 4));
-          if (t.stage == ST_GU && row < 8) u += co_loadf(p0, (uint32_t)(((size_t)k * 1024 + e + 8) * 4));
-        }
-        val[j] = v;
-        up[j] = u;
+        val[j] = 0.f;
+        up[j] = 0.f;
+      }
+      for (int k0 = 0; k0 < t.nks; k0 += kSumBatch) {
+        float pv[kSumBatch][4], pu[kSumBatch][4];
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = ((lane >> 4) + 4 * j) * 16 + row;
+            const bool ok = k0 + u < t.nks;
+            pv[u][j] = ok ? co_loadf(p0, (uint32_t)(((size_t)(k0 + u) * 1024 + e) * 4)) : 0.f;
+            pu[u][j] = ok && gu_up ? co_loadf(p0, (uint32_t)(((size_t)(k0 + u) * 1024 + e + 8) * 4)) : 0.f;
+          }
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            val[j] += pv[u][j];
+            up[j] += pu[u][j];
+          }
       }
       const int lr0 = tile_row0(0);
 #pragma unroll

@@ -49,9 +49,14 @@ int stage_k(const PlanCfg& p, int st) {
 //    to CUs as equal contiguous ranges; a CU's range is cut into tasks at
 //    row-group boundaries, and a row group whose K range is split over
 //    several CUs is finished by the last of its pieces.
-// The cheaper one (chunks streamed by the busiest CU, a split charged as
-// kSplitChunks chunks of extra latency) is chosen per stage.
+// The cheaper one is chosen per stage.  Costs are in units of one streamed
+// 16 KB weight chunk on the busiest CU: a split is charged kSplitChunks of
+// extra latency; staging the activation slice a task reads (b x K range,
+// 4 bytes per element in LDS) is charged per byte and per LDS window (each
+// window is a barrier plus a memory round trip while the ring sits full).
 constexpr int kSplitChunks = 6;
+constexpr double kStageChunksPerChunk = 0.5;  // staged activation bytes, per 16 KB
+constexpr double kWindowChunks = 4.0;         // per staged window
 
 struct Tiling {
   bool owner = false;
@@ -63,8 +68,15 @@ struct Tiling {
   long long ncols = 1;
 };
 
-Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw) {
+Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw, int b) {
   const int nst = (M + 15) / 16, nkb = (K + kKBlock - 1) / kKBlock;
+  // K blocks of one LDS staging window at this batch (the kernel's rule)
+  const int wkb = std::max(1, ((p.xb_bytes / (4 * b)) - 8) / kKBlock);
+  // staging cost of one task over `kbs` K blocks
+  auto stage_cost = [&](long long kbs) {
+    const long long windows = (kbs + wkb - 1) / wkb;
+    return (double)b * (double)kbs * kKBlock * 4.0 / kChunkBytes * kStageChunksPerChunk + (double)windows * kWindowChunks;
+  };
   Tiling best;
   best.nst = nst;
   best.nkb = nkb;
@@ -76,8 +88,10 @@ Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw) {
     t.ncols = (long long)t.ngroups * nkb;
     long long per_cu = (t.ncols + p.ncu - 1) / p.ncu;
     const bool split = (t.ncols % p.ncu) != 0 || ((t.ncols / p.ncu) % nkb) != 0;
+    // a CU's columns touch at least one group: one staged slice per group touched
+    const long long groups_cu = std::max(1LL, (per_cu + nkb - 1) / nkb);
     double cost = (double)per_cu * gs + 0.25 * (double)per_cu / nkb + (gs < kGroupSub ? 0.01 : 0.0) +
-                  (split ? kSplitChunks : 0);
+                  (split ? kSplitChunks : 0) + stage_cost(std::min<long long>(per_cu, nkb)) * (double)groups_cu;
     if (cost < best_cost) {
       best_cost = cost;
       best = t;
@@ -88,7 +102,10 @@ Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw) {
   own.tmax = 4 * tpw;
   const long long tiles_cu = (nst + p.ncu - 1) / p.ncu;
   const long long tasks_cu = (tiles_cu + own.tmax - 1) / own.tmax;
-  const double own_cost = (double)tiles_cu * nkb + 0.25 * (double)tasks_cu;
+  // a task whose full K fits one window reuses the slice staged by the CU's
+  // previous task; otherwise every task stages all its windows again
+  const double own_stage = stage_cost(nkb) * (double)(nkb <= wkb ? 1 : tasks_cu);
+  const double own_cost = (double)tiles_cu * nkb + 0.25 * (double)tasks_cu + own_stage;
   const bool use_owner = p.gemv_mode == 1 || (p.gemv_mode == 0 && own_cost <= best_cost);
   return use_owner ? own : best;
 }
@@ -156,7 +173,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   const int tpw = tiles_per_wave(mfma ? 0 : batch);
   for (int si = 0; si < 5; ++si) {
     int st = gemv_stages[si];
-    tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st), tpw);
+    tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st), tpw, batch);
     const Tiling& T = tl[st];
     P.stage_owner[st] = T.owner ? 1 : 0;
     if (T.owner) {
