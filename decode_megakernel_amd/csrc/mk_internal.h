@@ -31,14 +31,16 @@ constexpr int kGroupSub = 4;                 // 16-row sub-tiles per row group (
 // input staging buffer instead (the two never run at once), which needs
 // kAttnStateBytes of it.
 constexpr int kRedBytes = 4 * 256 * 4;
-// attention's use of the staging buffer (largest over head_dim 64 / group 8
-// and head_dim 128 / group 4): wave states (2 piece parities x 4 waves x
-// group x (hd + 4) fp32), per-wave queries (group x hd) and probabilities
-// (rows per chunk x 4 or 8 heads)
+// attention's use of the staging buffer: wave states (2 piece parities x
+// 4 waves x group x (hd + 4) fp32), the scaled queries and new K / V rows of
+// a batch of kAttnBatch pieces, per-wave transposed probabilities; largest
+// over head_dim 64 / group 8 and head_dim 128 / group 4
+constexpr int kAttnBatch = 4;
+constexpr int attn_lds_floats(int hd, int gm) {
+  return 2 * 4 * gm * (hd + 4) + kAttnBatch * gm * hd + kAttnBatch * 2 * hd + 4 * (4096 / hd) * gm;  // per wave: P^T as bf16 hi + lo, [group][rows per chunk] each
+}
 constexpr int kAttnStateBytes =
-    (2 * 4 * 8 * (64 + 4) + 4 * 8 * 64 + 4 * 64 * 8) * 4 > (2 * 4 * 4 * (128 + 4) + 4 * 4 * 128 + 4 * 32 * 4) * 4
-        ? (2 * 4 * 8 * (64 + 4) + 4 * 8 * 64 + 4 * 64 * 8) * 4
-        : (2 * 4 * 4 * (128 + 4) + 4 * 4 * 128 + 4 * 32 * 4) * 4;
+    4 * (attn_lds_floats(64, 8) > attn_lds_floats(128, 4) ? attn_lds_floats(64, 8) : attn_lds_floats(128, 4));
 constexpr int kStatWords = 64;               // trace: per-CU phase totals (uint64 words)
 #ifndef MK_PHASE_TRACE
 #define MK_PHASE_TRACE 0

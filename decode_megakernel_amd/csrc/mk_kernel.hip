@@ -1376,18 +1376,26 @@ __device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int la
 }
 
 // ---- attention --------------------------------------------------------
+// 2^x with the hardware instruction (about 1 ulp on normal results, 0 for
+// x = -inf, results below the normal range flush to 0: softmax weights that
+// small do not change a sum that holds a weight of 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct SoftState {
   float m, l;
 };
 
 // Load a head's 8 own elements and the 8 rotate-half partners of a raw q/k
 // row (fp32 in the qkv buffer), apply the optional per-head RMSNorm and RoPE.
+// `base` is wave-uniform; the head row starts `off` floats after it (the
+// offset may differ between lane groups).
 template <int HD>
-__device__ __forceinline__ void rope_head(DArgs A, const float* src /* head base */, const uint16_t* normw, int p, int e0, float* out) {
+__device__ __forceinline__ void rope_head(DArgs A, const float* base, uint32_t off, const uint16_t* normw, int p, int e0,
+                                          float* out) {
   constexpr int LPR = HD / 8;
-  u32x4 a0 = co_load16(src, (uint32_t)(e0 * 4)), a1 = co_load16(src, (uint32_t)((e0 + 4) * 4));
+  u32x4 a0 = co_load16(base, (off + e0) * 4), a1 = co_load16(base, (off + e0 + 4) * 4);
   const int pe = (e0 + HD / 2) % HD;
-  u32x4 b0 = co_load16(src, (uint32_t)(pe * 4)), b1 = co_load16(src, (uint32_t)((pe + 4) * 4));
+  u32x4 b0 = co_load16(base, (off + pe) * 4), b1 = co_load16(base, (off + pe + 4) * 4);
   float x[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
                 __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
   float y[8] = {__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
@@ -1435,7 +1443,6 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   constexpr int LPR = HD / 8, RP = 64 / LPR, RPC = 4096 / HD, NP = RPC / RP;
   constexpr int NRB = RPC / 16;        // 16-row blocks per chunk (MFMA N)
   constexpr int NDS = HD / 32;         // 32-wide steps over the head dimension (MFMA K)
-  constexpr int PH = GM <= 4 ? 4 : 8;  // heads per row of the probability buffer
   constexpr int SW = HD + 4;           // floats per head in a state / partial record
   constexpr float kLog2e = 1.4426950408889634f;
   const int l = t.layer, G = A->G, e0 = (lane % LPR) * 8, gi = lane / LPR;
@@ -1447,12 +1454,15 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   int qc = s.q, pidx = 0;
   const MK_AS4 LayerW& lw = as_const(A->layers)[l];
   // staging-buffer layout while attention runs: wave states (2 piece
-  // parities x 4 waves x GM x SW), then per wave the scaled queries (GM x HD)
-  // and the chunk's probabilities (RPC x PH)
+  // parities x 4 waves x GM x SW), the batch's scaled queries
+  // (kAttnBatch x GM x HD), its new K and V rows (kAttnBatch x 2 x HD), then
+  // per wave the chunk's transposed probabilities
   float* stb = (float*)xb_stage(A);
   const int stride_st = kComputeWaves * GM * SW;
-  float* qb = stb + 2 * stride_st + w * GM * HD;
-  float* pb = stb + 2 * stride_st + kComputeWaves * GM * HD + w * RPC * PH;
+  float* qs = stb + 2 * stride_st;
+  float* knv = qs + kAttnBatch * GM * HD;
+  float* pb = knv + kAttnBatch * 2 * HD + w * RPC * GM;  // P^T: 2 planes x GM heads x RPC bf16
+  const float* qkv_l = A->qkv + (size_t)l * A->bcap * A->nqkv;
   // trace: attention phase totals of compute wave 0 (per-CU stats words 32..41)
   uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0) ? MK_PSTAT(c, 0) : nullptr;
   uint64_t tlast = ast ? now_ticks() : 0;
@@ -1466,30 +1476,147 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   auto bcast = [](float v, int src_lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
   };
-  while (next_piece(c, A->b, A->nkv, RPC, pos, hi, P)) {
-    const int p = c->slen[P.i] - 1;
-    if (ast) trace_add(ast + 7, 1);
-    const float* qrow = A->qkv + ((size_t)l * A->bcap + P.i) * A->nqkv;
-    // queries: QK-norm + RoPE + scale (each lane group holds dims e0..e0+7),
-    // then this wave's copy in LDS re-read in the MFMA A layout
-    float q[GM][8];
+  // the finisher: compute wave w merges heads w, w + 4 of a segment from
+  // its pieces' partials; LPP lanes cover one piece's head vector, PPI
+  // pieces per pass; all loads of a batch are issued before any is used
+  struct Pend {
+    int sid, npieces, c_first, i, g;
+    long long seg_start;
+  };
+  const int pstride = GM * SW;
+  auto finish_segment = [&](const Pend& pd) {
+    const int sid = pd.sid, npieces = pd.npieces, c_first = pd.c_first;
+    const long long seg_start = pd.seg_start;
+    float* ob = A->attn_out + ((size_t)l * A->bcap + pd.i) * A->qdim + (size_t)pd.g * G * HD;
+    constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeIt = 16;
+    const int sub = lane / LPP, el = (lane % LPP) * 4;
+    auto piece_src = [&](int pc) -> const float* {
+      const int pcu = W >= A->ncu ? c_first + pc : cu_of(seg_start + pc, W, A->ncu);
+      return A->apart + (size_t)(pcu + sid) * pstride;
+    };
+    for (int h = w; h < G; h += kComputeWaves) {
+      float Mrun = -INFINITY, Lrun = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int p0 = 0; p0 < npieces; p0 += PPI * kMergeIt) {
+        u32x4 ov[kMergeIt];
+        float m2[kMergeIt], l2[kMergeIt];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        rope_head<HD>(A, qrow + (size_t)(P.g * G + h) * HD, A->qk_norm ? lw.q_norm : nullptr, p, e0, q[h]);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[h][u] *= qscale;
-        if (gi == 0) {
-          lds_st16((char*)(qb + h * HD + e0), u32x4{__float_as_uint(q[h][0]), __float_as_uint(q[h][1]),
-                                                    __float_as_uint(q[h][2]), __float_as_uint(q[h][3])});
-          lds_st16((char*)(qb + h * HD + e0 + 4), u32x4{__float_as_uint(q[h][4]), __float_as_uint(q[h][5]),
-                                                        __float_as_uint(q[h][6]), __float_as_uint(q[h][7])});
+        for (int k = 0; k < kMergeIt; ++k) {
+          const int pc = p0 + k * PPI + sub;
+          const float* src = piece_src(pc < npieces ? pc : 0);
+          ov[k] = co_load16(src, (uint32_t)((h * SW + el) * 4));
+          const u32x2 ml = co_load8(src, (uint32_t)((h * SW + HD) * 4));
+          m2[k] = pc < npieces ? __uint_as_float(ml.x) : -INFINITY;
+          l2[k] = __uint_as_float(ml.y);
         }
-      } else {
+        float mb = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) q[h][u] = 0.f;
+        for (int k = 0; k < kMergeIt; ++k) mb = fmaxf(mb, m2[k]);
+        mb = group_max<16>(mb);
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float mn = fmaxf(Mrun, mb);
+        const float fr = Mrun == -INFINITY ? 0.f : exp2f(Mrun - mn);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] *= fr;
+        Lrun *= fr;
+#pragma unroll
+        for (int k = 0; k < kMergeIt; ++k) {
+          const float f = m2[k] == -INFINITY ? 0.f : exp2f(m2[k] - mn);
+          acc[0] += f * __uint_as_float(ov[k].x);
+          acc[1] += f * __uint_as_float(ov[k].y);
+          acc[2] += f * __uint_as_float(ov[k].z);
+          acc[3] += f * __uint_as_float(ov[k].w);
+          Lrun += f * l2[k];
+        }
+        Mrun = mn;
+      }
+#pragma unroll
+      for (int msk = LPP; msk < 64; msk <<= 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] += __shfl_xor(acc[u], msk);
+        Lrun += __shfl_xor(Lrun, msk);
+      }
+      if (sub == 0) {
+        const float inv = 1.0f / Lrun;
+        co_store16(ob, (uint32_t)((h * HD + el) * 4),
+                   u32x4{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
+                         __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)});
       }
     }
+    if (ast) trace_add(ast + 8, 1);
+  };
+  long long bpos = pos;
+  while (bpos < hi) {
+    // ---- a batch of up to kAttnBatch pieces: first every query row (QK-norm,
+    // RoPE, scale) and every new K row (QK-norm, RoPE) and V row of the batch,
+    // one row per lane group, all loads in flight together; the new rows are
+    // rounded to bf16 and written to the cache here
+    int bi[kAttnBatch], bg[kAttnBatch], bnew[kAttnBatch], nbp = 0;
+    {
+      long long tpos = bpos;
+      Piece Q;
+#pragma unroll
+      for (int k = 0; k < kAttnBatch; ++k) {
+        bi[k] = bg[k] = bnew[k] = 0;
+        if (next_piece(c, A->b, A->nkv, RPC, tpos, hi, Q)) {
+          bi[k] = Q.i;
+          bg[k] = Q.g;
+          bnew[k] = Q.has_new;
+          nbp = k + 1;
+        }
+      }
+    }
+    const int nrows = nbp * (GM + 1);  // rows (piece, h): h < GM queries, h == GM the new K / V
+    for (int r0 = 0; r0 < nrows; r0 += kComputeWaves * RP) {
+      const int r = r0 + w * RP + gi;
+      const int k = r / (GM + 1), h = r - k * (GM + 1);
+      int pi = bi[0], pg = bg[0], pn = bnew[0];
+#pragma unroll
+      for (int kk = 1; kk < kAttnBatch; ++kk)
+        if (k == kk) {
+          pi = bi[kk];
+          pg = bg[kk];
+          pn = bnew[kk];
+        }
+      const bool is_k = h == GM;
+      const bool valid = r < nrows && (is_k ? pn != 0 : h < G);
+      const int pp = c->slen[pi] - 1;
+      const uint32_t rowoff = (uint32_t)pi * A->nqkv;
+      const uint32_t off = valid ? rowoff + (is_k ? A->qdim + pg * HD : (pg * G + h) * HD) : 0u;
+      const uint32_t voff = valid && is_k ? rowoff + A->qdim + A->kvdim + pg * HD : 0u;
+      const u32x4 v0 = co_load16(qkv_l, (voff + e0) * 4), v1 = co_load16(qkv_l, (voff + e0 + 4) * 4);
+      float x8[8];
+      rope_head<HD>(A, qkv_l, off, A->qk_norm ? (is_k ? lw.k_norm : lw.q_norm) : nullptr, valid ? pp : 0, e0, x8);
+      if (valid && !is_k) {
+        float* qd = qs + ((size_t)k * GM + h) * HD + e0;
+        lds_st16((char*)qd, u32x4{__float_as_uint(x8[0] * qscale), __float_as_uint(x8[1] * qscale),
+                                  __float_as_uint(x8[2] * qscale), __float_as_uint(x8[3] * qscale)});
+        lds_st16((char*)(qd + 4), u32x4{__float_as_uint(x8[4] * qscale), __float_as_uint(x8[5] * qscale),
+                                        __float_as_uint(x8[6] * qscale), __float_as_uint(x8[7] * qscale)});
+      }
+      if (valid && is_k) {
+        const u32x4 kb = {pack_bf2(x8[0], x8[1]), pack_bf2(x8[2], x8[3]), pack_bf2(x8[4], x8[5]), pack_bf2(x8[6], x8[7])};
+        const u32x4 vb = {pack_bf2(__uint_as_float(v0.x), __uint_as_float(v0.y)), pack_bf2(__uint_as_float(v0.z), __uint_as_float(v0.w)),
+                          pack_bf2(__uint_as_float(v1.x), __uint_as_float(v1.y)), pack_bf2(__uint_as_float(v1.z), __uint_as_float(v1.w))};
+        const size_t slot_row = ((((size_t)l * A->kv_bcap + pi) * A->nkv + pg) * A->kv_scap + pp) * HD + e0;
+        *(u32x4*)(A->kc + slot_row) = kb;
+        *(u32x4*)(A->vc + slot_row) = vb;
+        float kf[8], vf[8];
+        unpack8(kb, kf);
+        unpack8(vb, vf);
+        float* kd = knv + (size_t)k * 2 * HD + e0;
+        lds_st16((char*)kd, u32x4{__float_as_uint(kf[0]), __float_as_uint(kf[1]), __float_as_uint(kf[2]), __float_as_uint(kf[3])});
+        lds_st16((char*)(kd + 4), u32x4{__float_as_uint(kf[4]), __float_as_uint(kf[5]), __float_as_uint(kf[6]), __float_as_uint(kf[7])});
+        lds_st16((char*)(kd + HD), u32x4{__float_as_uint(vf[0]), __float_as_uint(vf[1]), __float_as_uint(vf[2]), __float_as_uint(vf[3])});
+        lds_st16((char*)(kd + HD + 4), u32x4{__float_as_uint(vf[4]), __float_as_uint(vf[5]), __float_as_uint(vf[6]), __float_as_uint(vf[7])});
+      }
+    }
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    for (int bk = 0; bk < nbp; ++bk) {
+    next_piece(c, A->b, A->nkv, RPC, bpos, hi, P);
+    if (ast) trace_add(ast + 7, 1);
+    const float* qk = qs + (size_t)bk * GM * HD;  // this piece's scaled queries
     u32x4 qa_hi[NDS], qa_lo[NDS];
     {
       const int kq = 8 * lr;
@@ -1497,19 +1624,29 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       for (int ds = 0; ds < NDS; ++ds) {
         qa_hi[ds] = qa_lo[ds] = u32x4{0, 0, 0, 0};
         if (r16 < G) {
-          const char* src = (const char*)(qb + r16 * HD + ds * 32 + kq);
+          const char* src = (const char*)(qk + r16 * HD + ds * 32 + kq);
           split8(lds_ld16(src), lds_ld16(src + 16), qa_hi[ds], qa_lo[ds]);
         }
       }
     }
-    float mrun[GM], lrun[GM], o[GM][8];
+    // output accumulators in the MFMA layout: lane holds heads 4 lr + i of
+    // dims nb * 16 + r16
+    constexpr int NB16 = HD / 16;  // 16-wide dim blocks (MFMA N of P.V)
+    constexpr int NKS = RPC / 32;  // 32-row steps of a chunk (MFMA K of P.V)
+    float mrun[GM], lrun[GM];
+    f32x4 O[NB16];
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       mrun[h] = -INFINITY;
       lrun[h] = 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) o[h][u] = 0.f;
     }
+#pragma unroll
+    for (int nb = 0; nb < NB16; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the value of a per-head wave-uniform array for this lane's head 4 lr + i
+    auto lane_head = [&](const float (&v)[GM], int i) { return (GM > 4 && lr == 1) ? v[(4 + i) % GM] : v[i % GM]; };
+    const int hsel = min(r16, GM - 1);  // A-operand rows past the group repeat its last head
+    uint16_t* pt_hi = (uint16_t*)pb;    // P^T [GM heads][RPC rows] as bf16 hi, then lo
+    uint16_t* pt_lo = pt_hi + GM * RPC;
     mark(0);
     // cached rows, streamed by the loader
     for (int ch = 0; ch < P.nch; ++ch) {
@@ -1550,116 +1687,131 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         mnew[h] = fmaxf(mrun[h], bcast(mx[h & 3], 16 * (h >> 2)));
-        fa[h] = mnew[h] == -INFINITY ? 1.f : exp2f(mrun[h] - mnew[h]);
+        fa[h] = mnew[h] == -INFINITY ? 1.f : fast_exp2(mrun[h] - mnew[h]);
       }
-      // probabilities of this lane's rows for its heads, row sums, to LDS
+      // probabilities of this lane's rows for its heads and their row sums;
+      // P^T to LDS as bf16 hi + lo planes (the A operand of P.V)
       float ls[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mh = (PH > 4 && lr == 1) ? mnew[(4 + i) % GM] : mnew[i % GM];
+        const float mh = lane_head(mnew, i);
+        const int hh = 4 * lr + i;
         float sum = 0.f;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          const float pv = S[rb][i] == -INFINITY ? 0.f : exp2f(S[rb][i] - mh);
-          S[rb][i] = pv;
+          // masked rows hold -inf and give exp2(-inf) = 0; mh is finite
+          // (every chunk has at least one row)
+          const float pv = fast_exp2(S[rb][i] - mh);
           sum += pv;
+          if (hh < GM) {
+            // hi = p truncated to bf16, lo = the remainder truncated to bf16
+            // (p in [0, 1]: the pair keeps p to about 2^-16)
+            const uint32_t bits = __float_as_uint(pv);
+            const float rem = pv - __uint_as_float(bits & 0xFFFF0000u);
+            pt_hi[hh * RPC + rb * 16 + r16] = (uint16_t)(bits >> 16);
+            pt_lo[hh * RPC + rb * 16 + r16] = (uint16_t)(__float_as_uint(rem) >> 16);
+          }
         }
         ls[i] = group_sum<16>(sum);
-      }
-      if (lr < PH / 4) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          lds_st16((char*)(pb + (rb * 16 + r16) * PH + 4 * lr),
-                   u32x4{__float_as_uint(S[rb][0]), __float_as_uint(S[rb][1]), __float_as_uint(S[rb][2]), __float_as_uint(S[rb][3])});
       }
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         lrun[h] = lrun[h] * fa[h] + bcast(ls[h & 3], 16 * (h >> 2));
         mrun[h] = mnew[h];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[h][u] *= fa[h];
       }
-      // V rows: lane group gi takes rows gi, gi + RP, ...
+      {
+        float fl[4];
 #pragma unroll
-      for (int pass = 0; pass < NP; ++pass) {
-        const int row = pass * RP + gi;
-        float vf[8], ph[PH];
-        unpack8(lds_ld16(slot + 8192 + (row * HD + e0) * 2), vf);
+        for (int i = 0; i < 4; ++i) fl[i] = lane_head(fa, i);
 #pragma unroll
-        for (int k = 0; k < PH / 4; ++k) {
-          const u32x4 pv = lds_ld16((const char*)(pb + row * PH + 4 * k));
-          ph[4 * k] = __uint_as_float(pv.x);
-          ph[4 * k + 1] = __uint_as_float(pv.y);
-          ph[4 * k + 2] = __uint_as_float(pv.z);
-          ph[4 * k + 3] = __uint_as_float(pv.w);
-        }
+        for (int nb = 0; nb < NB16; ++nb)
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          if (h >= G) continue;
+          for (int i = 0; i < 4; ++i) O[nb][i] *= fl[i];
+      }
+      // P.V on MFMA: A = P^T rows (heads) x 32 cached rows, B = 32 V rows x
+      // 16 dims gathered from the row-major chunk
+      const uint16_t* vrow = (const uint16_t*)(slot + 8192);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) o[h][u] += ph[h] * vf[u];
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int r0 = ks * 32 + 8 * lr;
+        const u32x4 ah = lds_ld16((const char*)(pt_hi + hsel * RPC + r0));
+        const u32x4 al = lds_ld16((const char*)(pt_lo + hsel * RPC + r0));
+#pragma unroll
+        for (int nb = 0; nb < NB16; ++nb) {
+          const uint16_t* vp = vrow + r0 * HD + nb * 16 + r16;
+          u32x4 bv;
+          bv.x = (uint32_t)vp[0] | ((uint32_t)vp[HD] << 16);
+          bv.y = (uint32_t)vp[2 * HD] | ((uint32_t)vp[3 * HD] << 16);
+          bv.z = (uint32_t)vp[4 * HD] | ((uint32_t)vp[5 * HD] << 16);
+          bv.w = (uint32_t)vp[6 * HD] | ((uint32_t)vp[7 * HD] << 16);
+          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al), __builtin_bit_cast(bf16x8_t, bv),
+                                                          O[nb], 0, 0, 0);
+          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bv),
+                                                          O[nb], 0, 0, 0);
         }
       }
       free_chunk(A, c, gq, lane);
     }
-    // the new row: K after QK-norm + RoPE, V raw, both rounded to bf16,
-    // written to the cache and absorbed by wave 0 (lane group 0 adds V)
+    // the new row (K, V rounded to bf16, already in the cache), absorbed by
+    // wave 0
     if (w == 0 && P.has_new) {
-      float kn[8], vn[8];
-      const float* krow = qrow + A->qdim + (size_t)P.g * HD;
-      const float* vrow = qrow + A->qdim + A->kvdim + (size_t)P.g * HD;
-      rope_head<HD>(A, krow, A->qk_norm ? lw.k_norm : nullptr, p, e0, kn);
-      u32x4 v0 = co_load16(vrow, (uint32_t)(e0 * 4)), v1 = co_load16(vrow, (uint32_t)((e0 + 4) * 4));
-      float vr[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
-                     __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
-      u32x4 kb = {pack_bf2(kn[0], kn[1]), pack_bf2(kn[2], kn[3]), pack_bf2(kn[4], kn[5]), pack_bf2(kn[6], kn[7])};
-      u32x4 vb = {pack_bf2(vr[0], vr[1]), pack_bf2(vr[2], vr[3]), pack_bf2(vr[4], vr[5]), pack_bf2(vr[6], vr[7])};
-      unpack8(kb, kn);
-      unpack8(vb, vn);
-      if (gi == 0) {
-        const size_t slot_row = ((((size_t)l * A->kv_bcap + P.i) * A->nkv + P.g) * A->kv_scap + p) * HD + e0;
-        *(u32x4*)(A->kc + slot_row) = kb;
-        *(u32x4*)(A->vc + slot_row) = vb;
+      const float* kd = knv + (size_t)bk * 2 * HD;
+      float kn[8];
+      {
+        const u32x4 k0 = lds_ld16((const char*)(kd + e0)), k1 = lds_ld16((const char*)(kd + e0 + 4));
+        kn[0] = __uint_as_float(k0.x); kn[1] = __uint_as_float(k0.y); kn[2] = __uint_as_float(k0.z); kn[3] = __uint_as_float(k0.w);
+        kn[4] = __uint_as_float(k1.x); kn[5] = __uint_as_float(k1.y); kn[6] = __uint_as_float(k1.z); kn[7] = __uint_as_float(k1.w);
       }
+      float fn[GM], pn[GM];
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
+        fn[h] = 1.f;
+        pn[h] = 0.f;
         if (h >= G) continue;
+        const float* qh = qk + h * HD + e0;
+        const u32x4 qa = lds_ld16((const char*)qh), qb2 = lds_ld16((const char*)(qh + 4));
+        const float qv[8] = {__uint_as_float(qa.x), __uint_as_float(qa.y), __uint_as_float(qa.z), __uint_as_float(qa.w),
+                             __uint_as_float(qb2.x), __uint_as_float(qb2.y), __uint_as_float(qb2.z), __uint_as_float(qb2.w)};
         float sc = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sc += q[h][u] * kn[u];
+        for (int u = 0; u < 8; ++u) sc += qv[u] * kn[u];
         sc = bcast(group_sum<LPR>(sc), 0);  // every lane group computed the same row
         const float mn = fmaxf(mrun[h], sc);
-        const float fa = exp2f(mrun[h] - mn), pw = exp2f(sc - mn);
-        lrun[h] = lrun[h] * fa + pw;
+        fn[h] = exp2f(mrun[h] - mn);
+        pn[h] = exp2f(sc - mn);
+        lrun[h] = lrun[h] * fn[h] + pn[h];
         mrun[h] = mn;
+      }
+      float fl[4], pl[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o[h][u] = o[h][u] * fa + (gi == 0 ? pw * vn[u] : 0.f);
+      for (int i = 0; i < 4; ++i) {
+        fl[i] = lane_head(fn, i);
+        pl[i] = lane_head(pn, i);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB16; ++nb) {
+        const float vv = kd[HD + nb * 16 + r16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[nb][i] = O[nb][i] * fl[i] + pl[i] * vv;
       }
     }
     mark(1);
-    // sum the lane groups (they share this wave's m), then wave state -> LDS
+    // wave state -> LDS
+    float* sb = stb + (pidx & 1) * stride_st + w * GM * SW;
 #pragma unroll
-    for (int msk = LPR; msk < 64; msk <<= 1) {
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * lr + i;
+      if (hh < G) {
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h >= G) continue;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[h][u] += __shfl_xor(o[h][u], msk);
+        for (int nb = 0; nb < NB16; ++nb) sb[hh * SW + nb * 16 + r16] = O[nb][i];
       }
     }
-    float* sb = stb + (pidx & 1) * stride_st + w * GM * SW;
-    if (gi == 0) {
+    if (lane == 0) {
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h >= G) continue;
-        lds_st16((char*)(sb + h * SW + e0), u32x4{__float_as_uint(o[h][0]), __float_as_uint(o[h][1]),
-                                                  __float_as_uint(o[h][2]), __float_as_uint(o[h][3])});
-        lds_st16((char*)(sb + h * SW + e0 + 4), u32x4{__float_as_uint(o[h][4]), __float_as_uint(o[h][5]),
-                                                      __float_as_uint(o[h][6]), __float_as_uint(o[h][7])});
-        if (lane == 0) {
-          sb[h * SW + HD] = mrun[h];
-          sb[h * SW + HD + 1] = lrun[h];
-        }
+        sb[h * SW + HD] = mrun[h];
+        sb[h * SW + HD + 1] = lrun[h];
       }
     }
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
@@ -1669,7 +1821,6 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     // CUs whose range is empty (fewer rows than CUs) hold no piece
     const int npieces = W >= A->ncu ? c_last - c_first + 1
                                    : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
-    const int pstride = GM * SW;
     float* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
     float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
     // merge the four wave states: wave w takes heads w, w + 4; each lane HD/64 dims
@@ -1717,72 +1868,14 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       }
       if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
       if (lds_ld_acq(&c->fin)) {
-        // compute wave w merges heads w, w + 4: LPP lanes cover one piece's
-        // head vector, PPI pieces per pass; all loads of a batch are issued
-        // before any is used
-        constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeIt = 16;
-        const int sub = lane / LPP, el = (lane % LPP) * 4;
-        auto piece_src = [&](int pc) -> const float* {
-          const int pcu = W >= A->ncu ? c_first + pc : cu_of(P.seg_start + pc, W, A->ncu);
-          return A->apart + (size_t)(pcu + P.sid) * pstride;
-        };
-        for (int h = w; h < G; h += kComputeWaves) {
-          float Mrun = -INFINITY, Lrun = 0.f;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          for (int p0 = 0; p0 < npieces; p0 += PPI * kMergeIt) {
-            u32x4 ov[kMergeIt];
-            float m2[kMergeIt], l2[kMergeIt];
-#pragma unroll
-            for (int k = 0; k < kMergeIt; ++k) {
-              const int pc = p0 + k * PPI + sub;
-              const float* src = piece_src(pc < npieces ? pc : 0);
-              ov[k] = co_load16(src, (uint32_t)((h * SW + el) * 4));
-              const u32x2 ml = co_load8(src, (uint32_t)((h * SW + HD) * 4));
-              m2[k] = pc < npieces ? __uint_as_float(ml.x) : -INFINITY;
-              l2[k] = __uint_as_float(ml.y);
-            }
-            float mb = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < kMergeIt; ++k) mb = fmaxf(mb, m2[k]);
-            mb = group_max<16>(mb);
-            mb = fmaxf(mb, __shfl_xor(mb, 16));
-            mb = fmaxf(mb, __shfl_xor(mb, 32));
-            const float mn = fmaxf(Mrun, mb);
-            const float fr = Mrun == -INFINITY ? 0.f : exp2f(Mrun - mn);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] *= fr;
-            Lrun *= fr;
-#pragma unroll
-            for (int k = 0; k < kMergeIt; ++k) {
-              const float f = m2[k] == -INFINITY ? 0.f : exp2f(m2[k] - mn);
-              acc[0] += f * __uint_as_float(ov[k].x);
-              acc[1] += f * __uint_as_float(ov[k].y);
-              acc[2] += f * __uint_as_float(ov[k].z);
-              acc[3] += f * __uint_as_float(ov[k].w);
-              Lrun += f * l2[k];
-            }
-            Mrun = mn;
-          }
-#pragma unroll
-          for (int msk = LPP; msk < 64; msk <<= 1) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] += __shfl_xor(acc[u], msk);
-            Lrun += __shfl_xor(Lrun, msk);
-          }
-          if (sub == 0) {
-            const float inv = 1.0f / Lrun;
-            co_store16(ob, (uint32_t)((h * HD + el) * 4),
-                       u32x4{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
-                             __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)});
-          }
-        }
+        finish_segment(Pend{P.sid, npieces, c_first, P.i, P.g, P.seg_start});
         mark(4);
-        if (ast) trace_add(ast + 8, 1);
       }
     }
     mark(5);
     qc += P.nch;
     ++pidx;
+    }
   }
   wait_mem();
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
