@@ -60,7 +60,7 @@ class PlanStats(ctypes.Structure):
 EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
            "mk_reset", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
-STAT_WORDS = 64  # per-CU trace totals, see mk_copy_trace
+STAT_WORDS = 80  # per-CU trace totals, see mk_copy_trace
 
 _lib = None
 

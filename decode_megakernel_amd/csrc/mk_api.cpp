@@ -93,6 +93,8 @@ static int check_cfg(const mk_model_cfg* c) {
   if (c->hidden % 64 || c->intermediate % 64) return MK_ERR_UNSUPPORTED;
   // the input staging sums at most 512 per-16-row partial sums of squares
   if (c->hidden > 8192) return MK_ERR_UNSUPPORTED;
+  // attention's flattened (sequence, KV head, position) rows are counted in 32 bits
+  if ((long long)c->n_kv_heads * c->max_batch * c->max_seq >= (1LL << 31)) return MK_ERR_UNSUPPORTED;
   // a K slice of one row of 16 bf16 columns per sequence must fit the staging buffer
   return MK_OK;
 }
@@ -352,6 +354,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   if (batch == 0) return MK_OK;
   if (!tokens || !positions || !seq_lens || !kv || !kv->k || !kv->v || !logits_out) return MK_ERR_INVALID_ARG;
   if (kv->batch_cap < batch || kv->seq_cap < 1) return MK_ERR_INVALID_ARG;
+  if ((long long)h->cfg.n_kv_heads * batch * kv->seq_cap >= (1LL << 31)) return MK_ERR_UNSUPPORTED;
   GraphDev* g = nullptr;
   int rc = get_graph(h, batch, &g);
   if (rc) return rc;

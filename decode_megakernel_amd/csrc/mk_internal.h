@@ -41,7 +41,7 @@ constexpr int attn_lds_floats(int hd, int gm) {
 }
 constexpr int kAttnStateBytes =
     4 * (attn_lds_floats(64, 8) > attn_lds_floats(128, 4) ? attn_lds_floats(64, 8) : attn_lds_floats(128, 4));
-constexpr int kStatWords = 64;               // trace: per-CU phase totals (uint64 words)
+constexpr int kStatWords = 80;               // trace: per-CU phase totals (uint64 words)
 #ifndef MK_PHASE_TRACE
 #define MK_PHASE_TRACE 0
 #endif

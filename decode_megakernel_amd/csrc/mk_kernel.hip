@@ -194,7 +194,7 @@ struct Ctrl {
   int tok[kMaxBatch];
   float rms[kMaxBatch];
 #if MK_PHASE_TRACE
-  uint64_t pstat[32];  // phase timers of compute wave 0, flushed at the end
+  uint64_t pstat[48];  // phase timers of compute wave 0, flushed at the end
 #endif
 };
 
@@ -427,10 +427,11 @@ __device__ __forceinline__ bool next_piece_r(const SeqLens& sl, int b, int nkv, 
       }
     }
   }
-  long long off = pos - acc;
+  // off < nkv * s < 2^31 (the host rejects larger caches): 32-bit division
+  const uint32_t off = (uint32_t)(pos - acc);
   P.i = i;
-  P.g = (int)(off / s);
-  P.j0 = (int)(off % s);
+  P.g = (int)(off / (uint32_t)s);
+  P.j0 = (int)(off - (uint32_t)P.g * (uint32_t)s);
   long long take = s - P.j0;
   if (hi - pos < take) take = hi - pos;
   P.j1 = P.j0 + (int)take;
@@ -472,10 +473,11 @@ __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rp
     acc += seg;
   }
   const int s = c->slen[i];
-  long long off = pos - acc;
+  // off < nkv * s < 2^31 (the host rejects larger caches): 32-bit division
+  const uint32_t off = (uint32_t)(pos - acc);
   P.i = i;
-  P.g = (int)(off / s);
-  P.j0 = (int)(off % s);
+  P.g = (int)(off / (uint32_t)s);
+  P.j0 = (int)(off - (uint32_t)P.g * (uint32_t)s);
   long long take = s - P.j0;
   if (hi - pos < take) take = hi - pos;
   P.j1 = P.j0 + (int)take;
@@ -808,8 +810,19 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
 __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int kk1, char* xb, Ctrl* c, CState& s, int w,
                             int lane) {
   if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == kk0 && s.x_k1 == kk1) return true;
+  // analysis builds: sub-phases of the QKV staging (compute wave 0)
+  uint64_t* sp = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0 && t.stage == ST_QKV) ? MK_PSTAT(c, 36) : nullptr;
+  uint64_t ts = sp ? now_ticks() : 0;
+  auto smark = [&](int k) {
+    if (sp) {
+      const uint64_t tn = now_ticks();
+      trace_add(sp + k, tn - ts);
+      ts = tn;
+    }
+  };
   // every compute wave must be done reading the previous slice
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  smark(0);
   // the fp32 input slice as bf16 hi and lo halves: [n][ksp] hi, then [n][ksp] lo
   const int K = stage_K(A, t.stage);
   const int ksl = kk1 - kk0, ksp = ksl + 8;
@@ -857,6 +870,7 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
       }
     }
   }
+  smark(1);
   if (rms) {
     for (int n = w; n < A->b; n += kComputeWaves) {
       float acc = 0.f;
@@ -878,7 +892,10 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   s.x_layer = t.layer;
   s.x_k0 = kk0;
   s.x_k1 = kk1;
-  return cbar(A, c, s.gen, lane, &s.w_bar);
+  smark(2);
+  const bool ok = cbar(A, c, s.gen, lane, &s.w_bar);
+  smark(3);
+  return ok;
 }
 
 // ---- VALU chunk: 16 rows x 512 K; lane l covers K elements [8l, 8l+8)
@@ -1546,6 +1563,16 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     }
     if (ast) trace_add(ast + 8, 1);
   };
+  // analysis builds: sub-phases of the query preparation (compute wave 0)
+  uint64_t* qsp = ast ? MK_PSTAT(c, 32) : nullptr;
+  uint64_t tq = qsp ? now_ticks() : 0;
+  auto qmark = [&](int k) {
+    if (qsp) {
+      const uint64_t tn = now_ticks();
+      trace_add(qsp + k, tn - tq);
+      tq = tn;
+    }
+  };
   long long bpos = pos;
   while (bpos < hi) {
     // ---- a batch of up to kAttnBatch pieces: first every query row (QK-norm,
@@ -1568,6 +1595,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       }
     }
     const int nrows = nbp * (GM + 1);  // rows (piece, h): h < GM queries, h == GM the new K / V
+    qmark(0);
     for (int r0 = 0; r0 < nrows; r0 += kComputeWaves * RP) {
       const int r = r0 + w * RP + gi;
       const int k = r / (GM + 1), h = r - k * (GM + 1);
@@ -1588,6 +1616,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       const u32x4 v0 = co_load16(qkv_l, (voff + e0) * 4), v1 = co_load16(qkv_l, (voff + e0 + 4) * 4);
       float x8[8];
       rope_head<HD>(A, qkv_l, off, A->qk_norm ? (is_k ? lw.k_norm : lw.q_norm) : nullptr, valid ? pp : 0, e0, x8);
+      qmark(1);
       if (valid && !is_k) {
         float* qd = qs + ((size_t)k * GM + h) * HD + e0;
         lds_st16((char*)qd, u32x4{__float_as_uint(x8[0] * qscale), __float_as_uint(x8[1] * qscale),
@@ -1612,7 +1641,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         lds_st16((char*)(kd + HD + 4), u32x4{__float_as_uint(vf[4]), __float_as_uint(vf[5]), __float_as_uint(vf[6]), __float_as_uint(vf[7])});
       }
     }
+    qmark(2);
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    qmark(3);
     for (int bk = 0; bk < nbp; ++bk) {
     next_piece(c, A->b, A->nkv, RPC, bpos, hi, P);
     if (ast) trace_add(ast + 7, 1);
@@ -1967,7 +1998,7 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
     if (w == 0) st[12] = now_ticks() - t_kernel0;
 #if MK_PHASE_TRACE
     if (w == 0)
-      for (int k = 0; k < 32; ++k) st[32 + k] = c->pstat[k];
+      for (int k = 0; k < 48; ++k) st[32 + k] = c->pstat[k];
 #endif
   }
   // Greedy tokens: once every LM task has signalled, the argmax keys are
@@ -2005,7 +2036,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
   }
   if (tid < kMaxBatch) c->lmkey[tid] = 0ull;
 #if MK_PHASE_TRACE
-  if (tid < 32) c->pstat[tid] = 0;
+  if (tid < 48) c->pstat[tid] = 0;
 #endif
   if (tid == 0) {
     c->dep = 0;

@@ -95,7 +95,8 @@ typedef struct {
   int32_t seq_cap;
 } mk_kv_cache;
 
-/* Create a handle: validates the shape, allocates the library-owned
+/* Create a handle: validates the shape (MK_ERR_UNSUPPORTED also when
+ * n_kv_heads x max_batch x max_seq reaches 2^31), allocates the library-owned
  * workspace (per-layer activations, partial sums, counters, RoPE table) on
  * the current HIP device.  *out is set only on success. */
 int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out);
@@ -111,7 +112,9 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
  *   next_tokens_out   device int32 [batch] greedy argmax (lowest index wins a
  *                     tie), written; may be NULL.
  * batch == 0 is a no-op.  Errors detectable on the host return an error code
- * before anything is enqueued; data errors are reported by mk_get_status. */
+ * before anything is enqueued (MK_ERR_UNSUPPORTED when n_kv_heads x batch x
+ * kv->seq_cap reaches 2^31: attention counts its rows in 32 bits); data
+ * errors are reported by mk_get_status. */
 int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
                    const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
                    int32_t* next_tokens_out, void* stream);
@@ -140,10 +143,10 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
 /* In-kernel trace (enabled when the environment variable MK_TRACE=<n> is set
  * at mk_create; otherwise *cap = 0 and nothing is copied).  Copies, enqueued
  * on `stream`, the trace of the last step into dst (device memory of at
- * least (n_cu*cap*4 + n_cu*64)*8 bytes): for each CU and each of its first
+ * least (n_cu*cap*4 + n_cu*80)*8 bytes): for each CU and each of its first
  * `cap` tasks, 4 uint64 words {task index << 32 | layer << 16 | type << 8 | stage,
  * begin, dependency satisfied, end} in s_memrealtime ticks (100 MHz); then
- * 64 uint64 per CU: [0..2] ticks the loader waves waited for a free LDS
+ * 80 uint64 per CU: [0..2] ticks the loader waves waited for a free LDS
  * slot, [4..7] the compute waves waited for a loaded chunk, [8..11] the
  * compute waves waited in barriers, [12] compute wave 0's total time, [13]
  * loader wave 0's total time, [16..19] compute chunk math, [20..23] GEMV
@@ -154,7 +157,10 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
  * pieces, [40] segments finished, [41] waits for cached rows; GEMV phases of
  * compute wave 0 summed over layers, at [42 + 4 s + k] for stage s (QKV 0,
  * LM head 1, O 2, gate/up 3, down 4) and k = 0 input staging, 1 streamed
- * chunks, 2 reductions and epilogue, 3 completion signal. */
+ * chunks, 2 reductions and epilogue, 3 completion signal; analysis builds
+ * only: attention query preparation at [64..67] (piece setup, loads and RoPE,
+ * LDS / cache stores, barrier) and QKV input staging at [68..71] (barrier,
+ * loads and split, RMS scales, barrier). */
 int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t* cap, void* stream);
 
 /* Synchronise `stream`, return the device status bits accumulated since the
