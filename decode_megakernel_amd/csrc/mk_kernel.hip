@@ -177,6 +177,7 @@ struct CState {
   int q;        // chunk sequence number of the current task's first chunk
   int last_dep; // counter of the last dependency already satisfied
   int x_stage, x_layer, x_k0, x_k1;  // signature of the staged input slice
+  int synced;   // every compute wave passed a barrier after its last read of the staging buffer
   int r_stage, r_layer;              // stage whose RMS scales are in Ctrl::rms
 };
 
@@ -820,8 +821,10 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
       ts = tn;
     }
   };
-  // every compute wave must be done reading the previous slice
-  if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  // every compute wave must be done reading the previous slice (already
+  // true right after a task that ended with a barrier)
+  if (!s.synced && !cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  s.synced = 0;
   smark(0);
   // the fp32 input slice as bf16 hi and lo halves: [n][ksp] hi, then [n][ksp] lo
   const int K = stage_K(A, t.stage);
@@ -1346,6 +1349,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   if (t.flags & kTaskSignal) {
     wait_mem();
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    s.synced = 1;
     if (w == 0) {
       if (t.stage == ST_LM && lane < A->b) {
         // fold this CU's argmax keys into the global ones
@@ -1388,6 +1392,7 @@ __device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int la
   if (valid && (tid & 3) == 0) co_storef(A->ssattn, (uint32_t)((((size_t)col >> 4) * A->bcap + n) * 4), ss);
   wait_mem();
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  s.synced = 1;
   if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   return true;
 }
@@ -1910,6 +1915,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   }
   wait_mem();
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  s.synced = 1;
   if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   mark(6);
   s.x_stage = -1;  // the staging buffer held softmax states
@@ -1946,7 +1952,7 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
   const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
   const int nt = as_const(A->task_off)[cu + 1] - as_const(A->task_off)[cu];
   CState& s = c->cs[w];
-  s = CState{0, 0, 0, 0, 0, 0, 0, 0, -1, -1, -1, -1, -1, -1, -1};
+  s = CState{0, 0, 0, 0, 0, 0, 0, 0, -1, -1, -1, -1, -1, -1, -1, 1};
   const uint64_t t_kernel0 = A->trace ? now_ticks() : 0;
   uint64_t* tr = (A->trace && w == 0 && lane == 0) ? A->trace + (size_t)cu * A->trace_cap * 4 : nullptr;
   const int rpc = 4096 / A->hd;
