@@ -464,6 +464,15 @@ __device__ __forceinline__ int cu_of(long long x, long long W, int ncu) {
   return (int)(((x + 1) * ncu + W - 1) / W) - 1;
 }
 
+// CUs that attention's rows are split over: every CU, except that a CU
+// takes at least kAttnMinRows rows, so that very short contexts are not cut
+// into many tiny pieces whose partials must all be merged.
+constexpr int kAttnMinRows = 32;
+__device__ __forceinline__ int attn_ncu(long long W, int ncu) {
+  const long long n = (W + kAttnMinRows - 1) / kAttnMinRows;
+  return n < 1 ? 1 : (n > ncu ? ncu : (int)n);
+}
+
 __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rpc, long long& pos, long long hi, Piece& P) {
   if (pos >= hi) return false;
   long long acc = 0;
@@ -704,8 +713,9 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
       qbase += nch;
     } else if (t.type == TT_ATTN) {
       const long long W = attn_total_r(sl, A->b, A->nkv);
-      long long pos = cu_lo(cu, W, A->ncu);
-      const long long hi = cu_lo(cu + 1, W, A->ncu);
+      const int nacu = attn_ncu(W, A->ncu);
+      long long pos = cu < nacu ? cu_lo(cu, W, nacu) : W;
+      const long long hi = cu < nacu ? cu_lo(cu + 1, W, nacu) : W;
       Piece P;
       int pbase = qbase;
       while (next_piece_r(sl, A->b, A->nkv, rpc, pos, hi, P)) {
@@ -740,7 +750,8 @@ __device__ __forceinline__ int attn_task_chunks(DArgs A, int cu, int rpc) {
   A = uni(A);
   const Ctrl* c = ctrl_block(A);
   long long W = attn_total(c, A->b, A->nkv);
-  long long pos = cu_lo(cu, W, A->ncu), hi = cu_lo(cu + 1, W, A->ncu);
+  const int nacu = attn_ncu(W, A->ncu);
+  long long pos = cu < nacu ? cu_lo(cu, W, nacu) : W, hi = cu < nacu ? cu_lo(cu + 1, W, nacu) : W;
   Piece P;
   int n = 0;
   while (next_piece(c, A->b, A->nkv, rpc, pos, hi, P)) n += P.nch;
@@ -1471,7 +1482,8 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   const int r16 = lane & 15, lr = lane >> 4;  // MFMA output layout: row r16 of a block, heads 4 lr + i
   const float qscale = kLog2e / sqrtf((float)HD);
   const long long W = attn_total(c, A->b, A->nkv);
-  long long pos = cu_lo(cu, W, A->ncu), hi = cu_lo(cu + 1, W, A->ncu);
+  const int nacu = attn_ncu(W, A->ncu);
+  long long pos = cu < nacu ? cu_lo(cu, W, nacu) : W, hi = cu < nacu ? cu_lo(cu + 1, W, nacu) : W;
   Piece P;
   int qc = s.q, pidx = 0;
   const MK_AS4 LayerW& lw = as_const(A->layers)[l];
@@ -1513,7 +1525,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeIt = 16;
     const int sub = lane / LPP, el = (lane % LPP) * 4;
     auto piece_src = [&](int pc) -> const float* {
-      const int pcu = W >= A->ncu ? c_first + pc : cu_of(seg_start + pc, W, A->ncu);
+      const int pcu = W >= nacu ? c_first + pc : cu_of(seg_start + pc, W, nacu);
       return A->apart + (size_t)(pcu + sid) * pstride;
     };
     for (int h = w; h < G; h += kComputeWaves) {
@@ -1853,10 +1865,10 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     mark(2);
     const int s_i = c->slen[P.i];
-    const int c_first = cu_of(P.seg_start, W, A->ncu), c_last = cu_of(P.seg_start + s_i - 1, W, A->ncu);
+    const int c_first = cu_of(P.seg_start, W, nacu), c_last = cu_of(P.seg_start + s_i - 1, W, nacu);
     // CUs whose range is empty (fewer rows than CUs) hold no piece
-    const int npieces = W >= A->ncu ? c_last - c_first + 1
-                                   : (int)(cu_lo(c_last + 1, W, A->ncu) - cu_lo(c_first, W, A->ncu));
+    const int npieces = W >= nacu ? c_last - c_first + 1
+                                   : (int)(cu_lo(c_last + 1, W, nacu) - cu_lo(c_first, W, nacu));
     float* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
     float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
     // merge the four wave states: wave w takes heads w, w + 4; each lane HD/64 dims
