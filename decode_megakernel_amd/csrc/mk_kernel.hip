@@ -1069,14 +1069,9 @@ __device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, i
     default: {  // LM head + greedy argmax
       float v = valid ? c->rms[n] * val : 0.f;
       if (valid) A->logits[(size_t)n * A->V + lr] = v;
-      unsigned long long key = valid ? argmax_key(v, lr) : 0ull;
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        unsigned long long o = ((unsigned long long)(uint32_t)__shfl_xor((int)(key >> 32), m) << 32) |
-                               (uint32_t)__shfl_xor((int)(uint32_t)key, m);
-        key = o > key ? o : key;
-      }
-      if (row == 0 && n < A->b && key) __hip_atomic_fetch_max(&c->lmkey[n], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // every lane folds its key into the CU's best key of sequence n (an
+      // LDS atomic max with no return: no wait, no cross-lane reduction)
+      if (valid) __hip_atomic_fetch_max(&c->lmkey[n], argmax_key(v, lr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       break;
     }
   }
@@ -1326,6 +1321,9 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], nwv[0], lane);
     }
   } else {
+    // analysis builds: LM-head epilogue split into tile reduction / epilogue
+    uint64_t* lsp = (MK_PHASE_TRACE && gst && t.stage == ST_LM) ? MK_PSTAT(c, 40) : nullptr;
+    uint64_t tl0 = lsp ? now_ticks() : 0;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       if (i >= nepi) break;
@@ -1352,8 +1350,18 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
           rs[j] = (has_resid && n < A->b && lr0 + row < M) ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4)) : 0.f;
         }
       }
+      if (lsp) {
+        const uint64_t tn = now_ticks();
+        trace_add(lsp, tn - tl0);
+        tl0 = tn;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], nw, lane);
+      if (lsp) {
+        const uint64_t tn = now_ticks();
+        trace_add(lsp + 1, tn - tl0);
+        tl0 = tn;
+      }
     }
   }
   gmark(2);
