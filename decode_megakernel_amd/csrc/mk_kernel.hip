@@ -816,6 +816,29 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
   return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// Lane exchanges across 16-lane rows with the VALU lane-swap instructions
+// (no LDS round trip).  permlane16_swap(a, b) returns ([a r0, b r0, a r2,
+// b r2], [a r1, b r1, a r3, b r3]) by 16-lane row; permlane32_swap(a, b)
+// returns ([a lo, b lo], [a hi, b hi]) by 32-lane half.  So x + y of a swap of
+// (a, b) is, on each lane, a + a' on the lower row (half) of a pair and
+// b + b' on the upper one, where ' is the partner lane (lane ^ 16 / ^ 32).
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float a) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float a) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---- stage the GEMV input slice x[n][kk0:kk1) (bf16, n < b) into LDS with
 //      rows padded to kk1-kk0+8 elements, and the RMS scales of stages that
 //      normalize their input.  Skipped when the same slice is already staged.
@@ -895,8 +918,8 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
         for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4));
       }
       acc = group_sum<16>(acc);
-      acc += __shfl_xor(acc, 16);
-      acc += __shfl_xor(acc, 32);
+      acc = swap16_sum(acc, acc);
+      acc = swap32_sum(acc, acc);
       if (lane == 0) c->rms[n] = 1.0f / sqrtf(acc / (float)A->d + A->eps);
     }
     s.r_stage = t.stage;
@@ -939,19 +962,13 @@ __device__ __forceinline__ void valu_reduce(float (&acc)[16][NB], int lane, floa
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     float v8[8], v4[4], v2[2], v1;
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+    const bool b3 = lane & 8, b2 = lane & 4;
+    // lane ^ 32: the lower half keeps rows r, the upper half rows r + 8
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float send = b5 ? acc[r][n] : acc[r + 8][n];
-      float keep = b5 ? acc[r + 8][n] : acc[r][n];
-      v8[r] = keep + __shfl_xor(send, 32);
-    }
+    for (int r = 0; r < 8; ++r) v8[r] = swap32_sum(acc[r][n], acc[r + 8][n]);
+    // lane ^ 16: even rows of 16 lanes keep r, odd ones r + 4
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float send = b4 ? v8[r] : v8[r + 4];
-      float keep = b4 ? v8[r + 4] : v8[r];
-      v4[r] = keep + __shfl_xor(send, 16);
-    }
+    for (int r = 0; r < 4; ++r) v4[r] = swap16_sum(v8[r], v8[r + 4]);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       float send = b3 ? v4[r] : v4[r + 2];
@@ -1555,8 +1572,8 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
 #pragma unroll
         for (int k = 0; k < kMergeIt; ++k) mb = fmaxf(mb, m2[k]);
         mb = group_max<16>(mb);
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        mb = swap16_max(mb);
+        mb = swap32_max(mb);
         const float mn = fmaxf(Mrun, mb);
         const float fr = Mrun == -INFINITY ? 0.f : exp2f(Mrun - mn);
 #pragma unroll
