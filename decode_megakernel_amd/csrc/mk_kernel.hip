@@ -1038,54 +1038,90 @@ __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int
   for (int q = 0; q < 4; ++q) acc[q] += alo[q];
 }
 
+// Where a GEMV stage's epilogue writes, computed once per task (wave-uniform
+// values, so the per-element code issues no kernel-argument loads).
+struct EpiCtx {
+  int stage, M, b, bcap, ostride;
+  float* out;    // QKV: qkv rows; O: mid-layer residual; DOWN: next residual; GU: SiLU·up; LM: logits
+  float* xo;     // O / DOWN: the next RMSNorm's input
+  float* ssout;  // O / DOWN: its per-16-row sums of squares
+};
+__device__ __forceinline__ EpiCtx make_epi(DArgs A, const Task& t) {
+  EpiCtx e;
+  const int l = t.layer;
+  e.stage = t.stage;
+  e.M = stage_M(A, t.stage);
+  e.b = A->b;
+  e.bcap = A->bcap;
+  e.xo = e.ssout = nullptr;
+  switch (t.stage) {
+    case ST_QKV:
+      e.out = A->qkv + (size_t)l * A->bcap * A->nqkv;
+      e.ostride = A->nqkv;
+      break;
+    case ST_O:
+      e.out = A->hmid + (size_t)l * A->bcap * A->d;
+      e.xo = A->xmlp + (size_t)l * A->bcap * A->d;
+      e.ssout = A->ssmlp + (size_t)l * (A->d / 16) * A->bcap;
+      e.ostride = A->d;
+      break;
+    case ST_DOWN:
+      e.out = A->hres + (size_t)(l + 1) * A->bcap * A->d;
+      e.xo = A->xattn + (size_t)(l + 1) * A->bcap * A->d;
+      e.ssout = A->ssattn + (size_t)(l + 1) * (A->d / 16) * A->bcap;
+      e.ostride = A->d;
+      break;
+    case ST_GU:
+      e.out = A->act + (size_t)l * A->bcap * A->I;
+      e.ostride = A->I;
+      break;
+    default:
+      e.out = A->logits;
+      e.ostride = A->V;
+      break;
+  }
+  return e;
+}
+
 // Epilogue of one output element (row `lr` of the stage, sequence n) of a
 // complete sub-tile.  Lanes map to (row = lane & 15, n), so each 16-lane
 // group holds one sequence's 16 consecutive rows.  `resid` is the residual
-// prefetched for O / DOWN.
-__device__ __forceinline__ void gemv_epilogue(DArgs A, const Task& t, Ctrl* c, int lr, int row, int n, float val, float val_up,
-                              float resid, float nw, int lane) {
-  const int l = t.layer;
-  const int M = stage_M(A, t.stage);
-  const bool valid = n < A->b && lr < M;
-  switch (t.stage) {
+// prefetched for O / DOWN, `nw` the next norm's weight of row lr, `rms` the
+// RMS scale of sequence n for the stages that normalise their input.
+__device__ __forceinline__ void gemv_epilogue(const EpiCtx& e, Ctrl* c, int lr, int row, int n, float val, float val_up,
+                                              float resid, float nw, float rms) {
+  const bool valid = n < e.b && lr < e.M;
+  const uint32_t off = (uint32_t)(((size_t)n * e.ostride + lr) * 4);
+  switch (e.stage) {
     case ST_QKV:
-      if (valid) co_storef(A->qkv, (uint32_t)((((size_t)l * A->bcap + n) * A->nqkv + lr) * 4), c->rms[n] * val);
+      if (valid) co_storef(e.out, off, rms * val);
       break;
     case ST_O:
     case ST_DOWN: {
       // h = residual + projection; also the next RMSNorm's input and its
       // per-16-row sum of squares.
-      const bool down = t.stage == ST_DOWN;
-      float* hout = down ? A->hres + (size_t)(l + 1) * A->bcap * A->d : A->hmid + (size_t)l * A->bcap * A->d;
-      float* xo = down ? A->xattn + (size_t)(l + 1) * A->bcap * A->d : A->xmlp + (size_t)l * A->bcap * A->d;
-      float* ssout = down ? A->ssattn + (size_t)(l + 1) * (A->d / 16) * A->bcap : A->ssmlp + (size_t)l * (A->d / 16) * A->bcap;
-      const uint32_t off = (uint32_t)(((size_t)n * A->d + lr) * 4);
       float h = valid ? resid + val : 0.f;
       const float xn = valid ? h * nw : 0.f;
       if (valid) {
-        co_storef(hout, off, h);
-        co_storef(xo, off, xn);
+        co_storef(e.out, off, h);
+        co_storef(e.xo, off, xn);
       }
       float ss = sum16(h * h);
-      if (valid && row == 0) co_storef(ssout, (uint32_t)((((size_t)lr >> 4) * A->bcap + n) * 4), ss);
+      if (valid && row == 0) co_storef(e.ssout, (uint32_t)((((size_t)lr >> 4) * e.bcap + n) * 4), ss);
       break;
     }
     case ST_GU: {
       // rows 0-7 of a 16-row logical tile are gate rows, 8-15 the same up rows
-      float a = 0.f;
       if (valid && row < 8) {
-        float g = c->rms[n] * val, u = c->rms[n] * val_up;
-        a = g / (1.0f + __expf(-g)) * u;
-      }
-      if (valid && row < 8) {
-        const int out = 8 * (lr >> 4) + row;
-        co_storef(A->act, (uint32_t)((((size_t)l * A->bcap + n) * A->I + out) * 4), a);
+        const float g = rms * val, u = rms * val_up;
+        const float a = g / (1.0f + __expf(-g)) * u;
+        co_storef(e.out, (uint32_t)(((size_t)n * e.ostride + 8 * (lr >> 4) + row) * 4), a);
       }
       break;
     }
     default: {  // LM head + greedy argmax
-      float v = valid ? c->rms[n] * val : 0.f;
-      if (valid) A->logits[(size_t)n * A->V + lr] = v;
+      const float v = valid ? rms * val : 0.f;
+      if (valid) e.out[(size_t)n * e.ostride + lr] = v;
       // every lane folds its key into the CU's best key of sequence n (an
       // LDS atomic max with no return: no wait, no cross-lane reduction)
       if (valid) __hip_atomic_fetch_max(&c->lmkey[n], argmax_key(v, lr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1256,21 +1292,55 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   // scratch (tile_values), then the leading wave of each sub-tile adds the
   // others' in a fixed order
   float sval[4] = {0.f, 0.f, 0.f, 0.f}, sup[4] = {0.f, 0.f, 0.f, 0.f};
+  // analysis builds: QKV reduction sub-phases (tile values, barrier, combine, epilogue)
+  uint64_t* rsp = (MK_PHASE_TRACE && gst && t.stage == ST_QKV) ? MK_PSTAT(c, 42) : nullptr;
+  uint64_t tr0 = rsp ? now_ticks() : 0;
+  auto rmark = [&](int k) {
+    if (rsp) {
+      const uint64_t tn = now_ticks();
+      trace_add(rsp + k, tn - tr0);
+      tr0 = tn;
+    }
+  };
   if (S > 1) {
     tile_values(0, sval, sup);
+    rmark(0);
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    rmark(1);
     if (lead) {
-      for (int k = 1; k < S; ++k) {
-        const float* ro = red + (w + nsub * k) * 256;
+      // every partial read first (one LDS wait), then summed in wave order
+      const bool gu = t.stage == ST_GU && row < 8;
+      float pv[kComputeWaves - 1][4], pu[kComputeWaves - 1][4];
+#pragma unroll
+      for (int k = 1; k < kComputeWaves; ++k) {
+        const float* ro = red + (w + nsub * (k < S ? k : 0)) * 256;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = (lane >> 4) + 4 * j;
-          sval[j] += ro[row * 16 + n];
-          if (t.stage == ST_GU && row < 8) sup[j] += ro[(row + 8) * 16 + n];
+          pv[k - 1][j] = ro[row * 16 + n];
+          pu[k - 1][j] = gu ? ro[(row + 8) * 16 + n] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 1; k < kComputeWaves; ++k) {
+        if (k >= S) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sval[j] += pv[k - 1][j];
+          sup[j] += pu[k - 1][j];
         }
       }
     }
   }
+  // epilogue targets and the RMS scales of this lane's sequences, once
+  const EpiCtx epi = make_epi(A, t);
+  float rmsv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = (lane >> 4) + 4 * j;
+    rmsv[j] = n < kMaxBatch ? c->rms[n] : 0.f;
+  }
+  rmark(2);
   auto owned_values = [&](int i, float (&val)[4], float (&up)[4]) {
     if (S > 1) {
 #pragma unroll
@@ -1335,7 +1405,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       }
       const int lr0 = tile_row0(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], nwv[0], lane);
+      for (int j = 0; j < 4; ++j) gemv_epilogue(epi, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], nwv[0], rmsv[j]);
     }
   } else {
     // analysis builds: LM-head epilogue split into tile reduction / epilogue
@@ -1373,7 +1443,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
         tl0 = tn;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gemv_epilogue(A, t, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], nw, lane);
+      for (int j = 0; j < 4; ++j) gemv_epilogue(epi, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], nw, rmsv[j]);
       if (lsp) {
         const uint64_t tn = now_ticks();
         trace_add(lsp + 1, tn - tl0);
@@ -1381,6 +1451,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       }
     }
   }
+  rmark(3);
   gmark(2);
   if (t.flags & kTaskSignal) {
     wait_mem();
