@@ -15,6 +15,8 @@
 
 namespace mk {
 hipError_t launch_step(const DevArgs& A, hipStream_t stream);
+hipError_t launch_untag_copy(void* dst, size_t dpitch, const void* src, size_t spitch, size_t row_bytes, size_t rows,
+                             hipStream_t stream);
 size_t lds_bytes(int nslot, int xb_bytes);
 }  // namespace mk
 
@@ -55,6 +57,8 @@ struct mk_handle {
   const uint16_t* final_norm = nullptr;
   char* ws = nullptr;
   size_t ws_bytes = 0;
+  size_t tagged_bytes = 0;  // leading workspace bytes whose words carry step tags
+  uint32_t rowtag = 0;      // bit n: the step tag sequence n's words carry now
   // workspace views
   float *hres, *hmid, *ssattn, *ssmlp, *qkv, *apart, *rope, *zero;
   float *xattn, *xmlp, *attn_out, *act;
@@ -219,6 +223,7 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   size_t o_rope = take((size_t)cfg->max_seq * (hd / 2) * 2 * 4);
   size_t o_zero = take(1024);
   h->ws_bytes = off;
+  h->tagged_bytes = o_apart;  // hres .. act: the activations consumers poll by tag
   if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
     delete h;
     return MK_ERR_OOM;
@@ -390,6 +395,9 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.next_tokens = next_tokens_out;
   A.b = batch;
   A.bank = (int)(h->step & 1);
+  // the sequences of this step flip their tag: words left by any earlier
+  // step carry the old value
+  A.rowtag = h->rowtag ^ ((1u << batch) - 1u);
   A.bcap = c.max_batch;
   A.hres = h->hres;
   A.hmid = h->hmid;
@@ -422,6 +430,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.trace = h->trace;
   A.trace_cap = h->trace_cap;
   if (launch_step(A, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  h->rowtag = A.rowtag;
   h->step += 1;
   return MK_OK;
 }
@@ -430,8 +439,8 @@ int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream) {
   if (!h || !dst || batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
   const size_t row = (size_t)batch * h->cfg.hidden * 4;
   const size_t spitch = (size_t)h->cfg.max_batch * h->cfg.hidden * 4;
-  if (hipMemcpy2DAsync(dst, row, h->hres, spitch, row, h->cfg.n_layers + 1, hipMemcpyDeviceToDevice,
-                       (hipStream_t)stream) != hipSuccess)
+  // copied with the step-tag bit cleared (bf16-exact values come back exact)
+  if (launch_untag_copy(dst, row, h->hres, spitch, row, h->cfg.n_layers + 1, (hipStream_t)stream) != hipSuccess)
     return MK_ERR_HIP;
   return MK_OK;
 }
@@ -451,9 +460,7 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
     default: return MK_ERR_INVALID_ARG;
   }
   const size_t row = (size_t)batch * width * esize, spitch = (size_t)c.max_batch * width * esize;
-  if (hipMemcpy2DAsync(dst, row, src, spitch, row, layers, hipMemcpyDeviceToDevice, (hipStream_t)stream) !=
-      hipSuccess)
-    return MK_ERR_HIP;
+  if (launch_untag_copy(dst, row, src, spitch, row, layers, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   return MK_OK;
 }
 
@@ -481,7 +488,11 @@ int mk_get_status(mk_handle* h, void* stream, uint32_t* status) {
 int mk_reset(mk_handle* h, void* stream) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
-  bool ok = hipMemset(h->banks, 0, (size_t)2 * h->bank_words * 4) == hipSuccess &&
+  // activations back to tag 0 everywhere, matching rowtag 0: an abandoned
+  // step may have left some words with a new tag
+  h->rowtag = 0;
+  bool ok = hipMemset(h->ws, 0, h->tagged_bytes) == hipSuccess &&
+            hipMemset(h->banks, 0, (size_t)2 * h->bank_words * 4) == hipSuccess &&
             hipMemset(h->seg_ctr, 0, (size_t)h->cfg.max_batch * h->cfg.n_kv_heads * 4) == hipSuccess &&
             hipMemset(h->status, 0, 8) == hipSuccess;
   for (auto& kv : h->graphs)

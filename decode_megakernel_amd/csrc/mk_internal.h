@@ -127,6 +127,7 @@ struct DevArgs {
   int32_t* next_tokens;
   int32_t b;
   int32_t bank;
+  uint32_t rowtag;      // bit n: step tag of sequence n (flipped each step it runs)
   // workspace (library-owned)
   int32_t bcap;         // workspace batch capacity
   float* hres;          // [L+1][bcap][d]

@@ -110,6 +110,30 @@ __device__ __forceinline__ void co_store4(void* base, uint32_t off, uint32_t v) 
 __device__ __forceinline__ float co_loadf(const void* base, uint32_t off) { return __uint_as_float(co_load4(base, off)); }
 __device__ __forceinline__ void co_storef(void* base, uint32_t off, float v) { co_store4(base, off, __float_as_uint(v)); }
 
+// ---- step tags.  Every fp32 word one stage hands to another (residual
+// stream, normalised inputs, sums of squares, q/k/v, attention outputs,
+// SiLU·up) carries in its least significant mantissa bit the step tag of its
+// sequence, which the host flips each step the sequence takes part in.  Each
+// 4-byte word is written once per step and read whole, so a consumer polls
+// the data itself until every word it needs carries this step's tag: no
+// store-completion wait and no counter on a hand-off.  Consumers clear the
+// bit before use (the value they see is the stored one truncated by at most
+// one ulp, whatever the tag), so results do not depend on the step's tag.
+__device__ __forceinline__ uint32_t tagged(float v, uint32_t tag) { return (__float_as_uint(v) & ~1u) | tag; }
+__device__ __forceinline__ bool tag_ok(uint32_t w, uint32_t tag) { return (w & 1u) == tag; }
+__device__ __forceinline__ bool tag_ok4(u32x4 v, uint32_t tag) {
+  const uint32_t all1 = v.x & v.y & v.z & v.w, any1 = v.x | v.y | v.z | v.w;
+  return ((tag ? all1 : any1) & 1u) == tag;
+}
+__device__ __forceinline__ void co_store_tag(void* base, uint32_t off, float v, uint32_t tag) {
+  co_store4(base, off, tagged(v, tag));
+}
+// Consumers use a tagged word with the bit cleared, so what they compute
+// does not depend on the step's tag value.
+__device__ __forceinline__ uint32_t untag(uint32_t w) { return w & ~1u; }
+__device__ __forceinline__ float untagf(float v) { return __uint_as_float(__float_as_uint(v) & ~1u); }
+__device__ __forceinline__ u32x4 untag4(u32x4 v) { return u32x4{v.x & ~1u, v.y & ~1u, v.z & ~1u, v.w & ~1u}; }
+
 __device__ __forceinline__ u32x4 nt_load16(const uint16_t* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
@@ -288,34 +312,6 @@ __device__ __forceinline__ uint32_t* bank_ptr(DArgs A, int which) {
 }
 __device__ __forceinline__ unsigned long long* keys_ptr(DArgs A) {
   return (unsigned long long*)(bank_ptr(A, A->bank) + kShards * A->ctr_stride);
-}
-
-// Wait (one wave, all 64 lanes) until every shard of counter `ctr` reached
-// the count the schedule expects.
-__device__ __forceinline__ bool wait_counter(DArgs A, Ctrl* c, int ctr, int lane) {
-  A = uni(A);
-  const uint32_t* p = bank_ptr(A, A->bank) + lane * A->ctr_stride + ctr;
-  const int e = as_const(A->expect)[ctr * kShards + lane];
-  const uint64_t t0 = now_ticks();
-  for (int it = 0;; ++it) {
-    int v = (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__all(v >= e)) return true;
-    if ((it & 15) == 15) {
-      if (global_aborted(A)) {
-        __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        return false;
-      }
-      if (now_ticks() - t0 > A->timeout_ticks) {
-        if (lane == 0) {
-          atomicOr(A->status, kStatusTimeout);
-          __hip_atomic_store(A->status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        return false;
-      }
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
 }
 
 __device__ __forceinline__ void signal_counter(DArgs A, int ctr, int cu) {
@@ -839,9 +835,35 @@ __device__ __forceinline__ float swap32_max(float a) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Sequence n's per-16-row partial sums of squares (nt <= 64 * kSsLoads of
+// them, entry lane + 64 k in u[k]), polled until each carries the sequence's
+// step tag.  `loaded`: u already holds a first attempt.  Entries past nt hold
+// the tag itself.
+constexpr int kSsLoads = 8;  // hidden <= 8192
+__device__ __forceinline__ bool poll_ss(DArgs A, Ctrl* c, const float* ss, int n, int nt, uint32_t tag, int lane,
+                                        uint32_t (&u)[kSsLoads], bool loaded) {
+  Spin sp = spin_start();
+  for (;;) {
+    if (!loaded) {
+#pragma unroll
+      for (int k = 0; k < kSsLoads; ++k) {
+        const int i = lane + 64 * k;
+        u[k] = i < nt ? co_load4(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4)) : tag;
+      }
+    }
+    loaded = false;
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < kSsLoads; ++k) ok = ok & tag_ok(u[k], tag);
+    if (__all(ok)) return true;
+    if (!spin_ok(A, c, sp)) return false;
+  }
+}
+
 // ---- stage the GEMV input slice x[n][kk0:kk1) (bf16, n < b) into LDS with
 //      rows padded to kk1-kk0+8 elements, and the RMS scales of stages that
 //      normalize their input.  Skipped when the same slice is already staged.
+//      The input words are polled until they carry the step tag.
 __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int kk1, char* xb, Ctrl* c, CState& s, int w,
                             int lane) {
   if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == kk0 && s.x_k1 == kk1) return true;
@@ -868,32 +890,46 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   const int per_row = ksl / 8;
   const int units = A->b * per_row;
   const int tid = w * 64 + lane;
-  // RMS partial sums of sequence w, loaded together with the input slice
+  const uint32_t tags = A->rowtag;
+  // RMS partial sums of sequence w, first attempt in flight with the input
   const float* ss = stage_ss(A, t.stage, t.layer);
   const bool rms = ss && !(s.r_stage == t.stage && s.r_layer == t.layer);
   const int nt = A->d / 16;
-  constexpr int kSsLoads = 8;  // d / 16 / 64 partials per lane (hidden <= 8192)
-  float ssv[kSsLoads];
+  const uint32_t tw = (tags >> w) & 1u;
+  uint32_t ssu[kSsLoads];
 #pragma unroll
   for (int k = 0; k < kSsLoads; ++k) {
     const int i = lane + 64 * k;
-    ssv[k] = (rms && w < A->b && i < nt) ? co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + w) * 4)) : 0.f;
+    ssu[k] = (rms && w < A->b && i < nt) ? co_load4(ss, (uint32_t)(((size_t)i * A->bcap + w) * 4)) : tw;
   }
   // up to kStageBatch units per thread in flight at once: one memory round
-  // trip per batch rather than per unit
+  // trip per batch rather than per unit; the batch is loaded again until
+  // every word carries its sequence's tag
   constexpr int kStageBatch = 4;
   for (int u0 = tid; u0 < units; u0 += kStageBatch * kComputeThreads) {
     u32x4 va[kStageBatch], vb[kStageBatch];
+    Spin sp = spin_start();
+    for (;;) {
+      bool ok = true;
 #pragma unroll
-    for (int k = 0; k < kStageBatch; ++k) {
-      const int u = u0 + k * kComputeThreads;
-      const int n = u / per_row, kq = u - n * per_row;
-      const uint32_t off = (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 4);
-      va[k] = vb[k] = u32x4{0, 0, 0, 0};
-      if (u < units) {
-        va[k] = co_load16(x, off);
-        vb[k] = co_load16(x, off + 16);
+      for (int k = 0; k < kStageBatch; ++k) {
+        const int u = u0 + k * kComputeThreads;
+        const int n = u / per_row, kq = u - n * per_row;
+        const uint32_t off = (uint32_t)(((size_t)n * K + kk0 + 8 * kq) * 4);
+        va[k] = vb[k] = u32x4{0, 0, 0, 0};
+        if (u < units) {
+          va[k] = co_load16(x, off);
+          vb[k] = co_load16(x, off + 16);
+        }
       }
+#pragma unroll
+      for (int k = 0; k < kStageBatch; ++k) {
+        const int u = u0 + k * kComputeThreads;
+        const uint32_t tg = (tags >> (u / per_row)) & 1u;
+        if (u < units) ok = ok & tag_ok4(va[k], tg) & tag_ok4(vb[k], tg);
+      }
+      if (__all(ok)) break;
+      if (!spin_ok(A, c, sp)) return false;
     }
 #pragma unroll
     for (int k = 0; k < kStageBatch; ++k) {
@@ -901,7 +937,7 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
       const int n = u / per_row, kq = u - n * per_row;
       if (u < units) {
         u32x4 hi, lo;
-        split8(va[k], vb[k], hi, lo);
+        split8(untag4(va[k]), untag4(vb[k]), hi, lo);
         lds_st16(xb + ((size_t)n * ksp + 8 * kq) * 2, hi);
         lds_st16(xlo + ((size_t)n * ksp + 8 * kq) * 2, lo);
       }
@@ -910,13 +946,10 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   smark(1);
   if (rms) {
     for (int n = w; n < A->b; n += kComputeWaves) {
+      if (!poll_ss(A, c, ss, n, nt, (tags >> n) & 1u, lane, ssu, n == w)) return false;
       float acc = 0.f;
-      if (n == w) {
 #pragma unroll
-        for (int k = 0; k < kSsLoads; ++k) acc += ssv[k];
-      } else {
-        for (int i = lane; i < nt; i += 64) acc += co_loadf(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4));
-      }
+      for (int k = 0; k < kSsLoads; ++k) acc += lane + 64 * k < nt ? __uint_as_float(untag(ssu[k])) : 0.f;
       acc = group_sum<16>(acc);
       acc = swap16_sum(acc, acc);
       acc = swap32_sum(acc, acc);
@@ -1042,6 +1075,7 @@ __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int
 // values, so the per-element code issues no kernel-argument loads).
 struct EpiCtx {
   int stage, M, b, bcap, ostride;
+  uint32_t tags;  // per-sequence step tags of the stored words
   float* out;    // QKV: qkv rows; O: mid-layer residual; DOWN: next residual; GU: SiLU·up; LM: logits
   float* xo;     // O / DOWN: the next RMSNorm's input
   float* ssout;  // O / DOWN: its per-16-row sums of squares
@@ -1053,6 +1087,7 @@ __device__ __forceinline__ EpiCtx make_epi(DArgs A, const Task& t) {
   e.M = stage_M(A, t.stage);
   e.b = A->b;
   e.bcap = A->bcap;
+  e.tags = A->rowtag;
   e.xo = e.ssout = nullptr;
   switch (t.stage) {
     case ST_QKV:
@@ -1092,9 +1127,10 @@ __device__ __forceinline__ void gemv_epilogue(const EpiCtx& e, Ctrl* c, int lr, 
                                               float resid, float nw, float rms) {
   const bool valid = n < e.b && lr < e.M;
   const uint32_t off = (uint32_t)(((size_t)n * e.ostride + lr) * 4);
+  const uint32_t tg = (e.tags >> n) & 1u;
   switch (e.stage) {
     case ST_QKV:
-      if (valid) co_storef(e.out, off, rms * val);
+      if (valid) co_store_tag(e.out, off, rms * val, tg);
       break;
     case ST_O:
     case ST_DOWN: {
@@ -1103,11 +1139,11 @@ __device__ __forceinline__ void gemv_epilogue(const EpiCtx& e, Ctrl* c, int lr, 
       float h = valid ? resid + val : 0.f;
       const float xn = valid ? h * nw : 0.f;
       if (valid) {
-        co_storef(e.out, off, h);
-        co_storef(e.xo, off, xn);
+        co_store_tag(e.out, off, h, tg);
+        co_store_tag(e.xo, off, xn, tg);
       }
       float ss = sum16(h * h);
-      if (valid && row == 0) co_storef(e.ssout, (uint32_t)((((size_t)lr >> 4) * e.bcap + n) * 4), ss);
+      if (valid && row == 0) co_store_tag(e.ssout, (uint32_t)((((size_t)lr >> 4) * e.bcap + n) * 4), ss, tg);
       break;
     }
     case ST_GU: {
@@ -1115,7 +1151,7 @@ __device__ __forceinline__ void gemv_epilogue(const EpiCtx& e, Ctrl* c, int lr, 
       if (valid && row < 8) {
         const float g = rms * val, u = rms * val_up;
         const float a = g / (1.0f + __expf(-g)) * u;
-        co_storef(e.out, (uint32_t)(((size_t)n * e.ostride + 8 * (lr >> 4) + row) * 4), a);
+        co_store_tag(e.out, (uint32_t)(((size_t)n * e.ostride + 8 * (lr >> 4) + row) * 4), a, tg);
       }
       break;
     }
@@ -1258,12 +1294,37 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   gmark(1);
   // Land the prefetched residuals and norm weights now, while no store is in
   // flight: a first use after the epilogue's stores would make the wait on
-  // them also wait for those stores.
+  // them also wait for those stores.  Residual words without this step's tag
+  // are loaded again.
 #pragma unroll
-  for (int i = 0; i < kResidTiles; ++i) {
-    asm volatile("" ::"v"(nwv[i]));
+  for (int i = 0; i < kResidTiles; ++i) asm volatile("" ::"v"(nwv[i]));
+  if (has_resid && lead) {
+    const uint32_t tags = A->rowtag;
+    Spin sp = spin_start();
+    for (;;) {
+      bool ok = true;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(resid[i][j]));
+      for (int i = 0; i < kResidTiles; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = (lane >> 4) + 4 * j;
+          if (i < nown && n < A->b && tile_row0(i) + row < M)
+            ok = ok & tag_ok(__float_as_uint(resid[i][j]), (tags >> n) & 1u);
+        }
+      if (__all(ok)) break;
+      if (!spin_ok(A, c, sp)) return false;
+#pragma unroll
+      for (int i = 0; i < kResidTiles; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = (lane >> 4) + 4 * j, lr = tile_row0(i) + row;
+          if (i < nown && n < A->b && lr < M) resid[i][j] = co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kResidTiles; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) resid[i][j] = untagf(resid[i][j]);
   }
   // owned sub-tile i's totals -> this wave's LDS scratch as [16 rows][16 n],
   // read back with lanes mapped to (row = lane & 15, n = lane / 16 + 4 j)
@@ -1428,14 +1489,30 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
       static_assert(kResidTiles == 2, "prefetched tiles are selected by constant index");
       const float nw = i == 0 ? nwv[0] : (i == 1 ? nwv[1] : ((has_resid && lr0 + row < M) ? bf2f(nwp[lr0 + row]) : 0.f));
       float rs[4];
+      if (i < kResidTiles) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (i < kResidTiles) {
-          rs[j] = i == 0 ? resid[0][j] : resid[1][j];
-        } else {
-          const int n = (lane >> 4) + 4 * j;
-          rs[j] = (has_resid && n < A->b && lr0 + row < M) ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4)) : 0.f;
+        for (int j = 0; j < 4; ++j) rs[j] = i == 0 ? resid[0][j] : resid[1][j];
+      } else if (has_resid) {
+        // residuals of tiles past the prefetched ones, polled for their tags
+        const uint32_t tags = A->rowtag;
+        Spin sp = spin_start();
+        for (;;) {
+          bool ok = true;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = (lane >> 4) + 4 * j;
+            const bool need = n < A->b && lr0 + row < M;
+            rs[j] = need ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr0 + row) * 4)) : 0.f;
+            if (need) ok = ok & tag_ok(__float_as_uint(rs[j]), (tags >> n) & 1u);
+          }
+          if (__all(ok)) break;
+          if (!spin_ok(A, c, sp)) return false;
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rs[j] = untagf(rs[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rs[j] = 0.f;
       }
       if (lsp) {
         const uint64_t tn = now_ticks();
@@ -1454,11 +1531,15 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   rmark(3);
   gmark(2);
   if (t.flags & kTaskSignal) {
-    wait_mem();
+    // the last task of its stage on this CU.  Consumers poll the tagged
+    // outputs, so only the LM head counts its completed tasks (for the
+    // greedy tokens).
+    const bool lm = t.stage == ST_LM;
+    if (lm) wait_mem();
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     s.synced = 1;
-    if (w == 0) {
-      if (t.stage == ST_LM && lane < A->b) {
+    if (lm && w == 0) {
+      if (lane < A->b) {
         // fold this CU's argmax keys into the global ones
         const unsigned long long key = c->lmkey[lane];
         if (key) __hip_atomic_fetch_max(keys_ptr(A) + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1482,25 +1563,25 @@ __device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int la
   const int tid = w * 64 + lane, n = tid >> 4, col = t.row0 + 4 * (tid & 15);
   float h[4] = {0.f, 0.f, 0.f, 0.f};
   const bool valid = n < A->b;
+  const uint32_t tg = (A->rowtag >> n) & 1u;
   if (valid) {
     const uint16_t* e = A->embed + (size_t)c->tok[n] * A->d + col;
     u32x2 ev = *(const u32x2*)e;
     h[0] = bf_lo(ev.x); h[1] = bf_hi(ev.x); h[2] = bf_lo(ev.y); h[3] = bf_hi(ev.y);
     const uint16_t* nw = as_const(A->layers)[0].attn_norm + col;
     co_store16(A->hres, (uint32_t)(((size_t)n * A->d + col) * 4),
-               u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
+               u32x4{tagged(h[0], tg), tagged(h[1], tg), tagged(h[2], tg), tagged(h[3], tg)});
     co_store16(A->xattn, (uint32_t)(((size_t)n * A->d + col) * 4),
-               u32x4{__float_as_uint(h[0] * bf2f(nw[0])), __float_as_uint(h[1] * bf2f(nw[1])),
-                     __float_as_uint(h[2] * bf2f(nw[2])), __float_as_uint(h[3] * bf2f(nw[3]))});
+               u32x4{tagged(h[0] * bf2f(nw[0]), tg), tagged(h[1] * bf2f(nw[1]), tg),
+                     tagged(h[2] * bf2f(nw[2]), tg), tagged(h[3] * bf2f(nw[3]), tg)});
   }
   float ss = h[0] * h[0] + h[1] * h[1] + h[2] * h[2] + h[3] * h[3];
   ss += __shfl_xor(ss, 1);
   ss += __shfl_xor(ss, 2);
-  if (valid && (tid & 3) == 0) co_storef(A->ssattn, (uint32_t)((((size_t)col >> 4) * A->bcap + n) * 4), ss);
-  wait_mem();
+  if (valid && (tid & 3) == 0) co_store_tag(A->ssattn, (uint32_t)((((size_t)col >> 4) * A->bcap + n) * 4), ss, tg);
+  // consumers poll the tagged words: no completion wait, no counter
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   s.synced = 1;
-  if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   return true;
 }
 
@@ -1514,17 +1595,14 @@ struct SoftState {
   float m, l;
 };
 
-// Load a head's 8 own elements and the 8 rotate-half partners of a raw q/k
-// row (fp32 in the qkv buffer), apply the optional per-head RMSNorm and RoPE.
-// `base` is wave-uniform; the head row starts `off` floats after it (the
-// offset may differ between lane groups).
+// A head's 8 own elements (a0, a1: elements e0..e0+7) and their 8
+// rotate-half partners (b0, b1) of a raw q/k row: apply the optional per-head
+// RMSNorm and RoPE at position p.
 template <int HD>
-__device__ __forceinline__ void rope_head(DArgs A, const float* base, uint32_t off, const uint16_t* normw, int p, int e0,
-                                          float* out) {
+__device__ __forceinline__ void rope_head(DArgs A, u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, const uint16_t* normw, int p,
+                                          int e0, float* out) {
   constexpr int LPR = HD / 8;
-  u32x4 a0 = co_load16(base, (off + e0) * 4), a1 = co_load16(base, (off + e0 + 4) * 4);
   const int pe = (e0 + HD / 2) % HD;
-  u32x4 b0 = co_load16(base, (off + pe) * 4), b1 = co_load16(base, (off + pe + 4) * 4);
   float x[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
                 __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
   float y[8] = {__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
@@ -1593,6 +1671,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   float* knv = qs + kAttnBatch * GM * HD;
   float* pb = knv + kAttnBatch * 2 * HD + w * RPC * GM;  // P^T: 2 planes x GM heads x RPC bf16
   const float* qkv_l = A->qkv + (size_t)l * A->bcap * A->nqkv;
+  const uint32_t tags = A->rowtag;
   // trace: attention phase totals of compute wave 0 (per-CU stats words 32..41)
   uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0) ? MK_PSTAT(c, 0) : nullptr;
   uint64_t tlast = ast ? now_ticks() : 0;
@@ -1669,9 +1748,10 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       }
       if (sub == 0) {
         const float inv = 1.0f / Lrun;
+        const uint32_t tg = (tags >> pd.i) & 1u;
         co_store16(ob, (uint32_t)((h * HD + el) * 4),
-                   u32x4{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
-                         __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)});
+                   u32x4{tagged(acc[0] * inv, tg), tagged(acc[1] * inv, tg), tagged(acc[2] * inv, tg),
+                         tagged(acc[3] * inv, tg)});
       }
     }
     if (ast) trace_add(ast + 8, 1);
@@ -1726,9 +1806,34 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       const uint32_t rowoff = (uint32_t)pi * A->nqkv;
       const uint32_t off = valid ? rowoff + (is_k ? A->qdim + pg * HD : (pg * G + h) * HD) : 0u;
       const uint32_t voff = valid && is_k ? rowoff + A->qdim + A->kvdim + pg * HD : 0u;
-      const u32x4 v0 = co_load16(qkv_l, (voff + e0) * 4), v1 = co_load16(qkv_l, (voff + e0 + 4) * 4);
+      // the head's elements, their rotate-half partners and (new rows) the V
+      // row, loaded again until every word carries the sequence's step tag
+      const int pe = (e0 + HD / 2) % HD;
+      const uint32_t tg = (tags >> pi) & 1u;
+      u32x4 a0, a1, b0, b1, v0, v1;
+      {
+        Spin sp = spin_start();
+        for (;;) {
+          a0 = co_load16(qkv_l, (off + e0) * 4);
+          a1 = co_load16(qkv_l, (off + e0 + 4) * 4);
+          b0 = co_load16(qkv_l, (off + pe) * 4);
+          b1 = co_load16(qkv_l, (off + pe + 4) * 4);
+          v0 = co_load16(qkv_l, (voff + e0) * 4);
+          v1 = co_load16(qkv_l, (voff + e0 + 4) * 4);
+          const bool ok = !valid || (tag_ok4(a0, tg) & tag_ok4(a1, tg) & tag_ok4(b0, tg) & tag_ok4(b1, tg) &
+                                     (!is_k || (tag_ok4(v0, tg) & tag_ok4(v1, tg))));
+          if (__all(ok)) break;
+          if (!spin_ok(A, c, sp)) return false;
+        }
+        a0 = untag4(a0);
+        a1 = untag4(a1);
+        b0 = untag4(b0);
+        b1 = untag4(b1);
+        v0 = untag4(v0);
+        v1 = untag4(v1);
+      }
       float x8[8];
-      rope_head<HD>(A, qkv_l, off, A->qk_norm ? (is_k ? lw.k_norm : lw.q_norm) : nullptr, valid ? pp : 0, e0, x8);
+      rope_head<HD>(A, a0, a1, b0, b1, A->qk_norm ? (is_k ? lw.k_norm : lw.q_norm) : nullptr, valid ? pp : 0, e0, x8);
       qmark(1);
       if (valid && !is_k) {
         float* qd = qs + ((size_t)k * GM + h) * HD + e0;
@@ -1989,8 +2094,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       if (npieces == 1) {
         // the whole segment is here: normalise and store
         const float inv = 1.0f / L;
-        if constexpr (DPL == 2) co_store8(ob, (uint32_t)((h * HD + 2 * lane) * 4), u32x2{__float_as_uint(O[0] * inv), __float_as_uint(O[1] * inv)});
-        else co_storef(ob, (uint32_t)((h * HD + lane) * 4), O[0] * inv);
+        const uint32_t tg = (tags >> P.i) & 1u;
+        if constexpr (DPL == 2) co_store8(ob, (uint32_t)((h * HD + 2 * lane) * 4), u32x2{tagged(O[0] * inv, tg), tagged(O[1] * inv, tg)});
+        else co_store_tag(ob, (uint32_t)((h * HD + lane) * 4), O[0] * inv, tg);
       } else {
         if constexpr (DPL == 2) co_store8(dst, (uint32_t)((h * SW + 2 * lane) * 4), u32x2{__float_as_uint(O[0]), __float_as_uint(O[1])});
         else co_storef(dst, (uint32_t)((h * SW + lane) * 4), O[0]);
@@ -2021,10 +2127,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     ++pidx;
     }
   }
-  wait_mem();
+  // the O projection polls the tagged outputs: no completion wait, no counter
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   s.synced = 1;
-  if (w == 0 && lane == 0) signal_counter(A, t.signal_ctr, cu);
   mark(6);
   s.x_stage = -1;  // the staging buffer held softmax states
   return true;
@@ -2068,18 +2173,9 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
   for (int ti = 0; ti < nt; ++ti) {
     const Task t = load_task(uni(T + ti));
     const uint64_t t_begin = tr ? now_ticks() : 0;
-    if (t.wait_ctr >= 0 && t.wait_ctr != s.last_dep) {
-      if (w == 0) {
-        if (!wait_counter(A, c, t.wait_ctr, lane)) return;
-        if (lane == 0) lds_st_rel(&c->dep, ti + 1);
-      } else {
-        Spin sp = spin_start();
-        while (lds_ld_acq(&c->dep) < ti + 1)
-          if (!spin_ok(A, c, sp)) return;
-      }
-      s.last_dep = t.wait_ctr;
-    }
-    const uint64_t t_dep = tr ? now_ticks() : 0;
+    // no wait here: a task polls its tagged inputs itself (the schedule's
+    // dependency counters order the streams and are checked on the host)
+    const uint64_t t_dep = t_begin;
     s.t_stream = 0;
     bool ok;
     int nch = 0;
@@ -2196,6 +2292,27 @@ hipError_t launch_step(const DevArgs& A, hipStream_t stream) {
     lds_set = lds;
   }
   hipLaunchKernelGGL(mk_step_kernel, dim3(A.ncu), dim3(kThreads), lds, stream, A);
+  return hipGetLastError();
+}
+
+// Copy of `rows` rows of 32-bit activation words with the step-tag bit
+// cleared (pitches and row length in bytes, multiples of 4).
+__global__ void mk_untag_copy_kernel(uint32_t* dst, size_t dpitch, const uint32_t* src, size_t spitch, size_t words,
+                                     size_t rows) {
+  const size_t total = words * rows;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / words, k = i - r * words;
+    dst[r * dpitch + k] = src[r * spitch + k] & ~1u;
+  }
+}
+
+hipError_t launch_untag_copy(void* dst, size_t dpitch, const void* src, size_t spitch, size_t row_bytes, size_t rows,
+                             hipStream_t stream) {
+  const size_t words = row_bytes / 4, total = words * rows;
+  if (total == 0) return hipSuccess;
+  const size_t blocks = (total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096;
+  hipLaunchKernelGGL(mk_untag_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint32_t*)dst, dpitch / 4,
+                     (const uint32_t*)src, spitch / 4, words, rows);
   return hipGetLastError();
 }
 

@@ -121,12 +121,16 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
 
 /* Copy the residual stream of the last step, enqueued on `stream`:
  * dst [n_layers+1][batch][hidden] float, entry l = input of layer l (entry 0
- * is the gathered embedding, entry n_layers leaves the last layer). */
+ * is the gathered embedding, entry n_layers leaves the last layer).  The
+ * kernel hands activations between compute units with a step tag in each
+ * fp32 word's least significant mantissa bit; copies come back with that bit
+ * cleared, the value every consumer inside the step used (so the gathered
+ * bf16 embedding rows come back exactly). */
 int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream);
 
 /* Copy one per-layer mid-state buffer of the last step, enqueued on
  * `stream`, for sequences 0..batch-1 of every layer, into dst (layout
- * [layers][batch][width], dtype as listed):
+ * [layers][batch][width], dtype as listed; tag bit cleared as above):
  *   MK_STATE_HIDDEN   float, L+1 layers, width hidden (same as mk_copy_hidden)
  *   MK_STATE_HMID     float, L, hidden: residual after attention + O proj
  *   MK_STATE_QKV      float, L, (n_q+2 n_kv) head_dim: raw q|k|v projections
@@ -145,7 +149,8 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
  * on `stream`, the trace of the last step into dst (device memory of at
  * least (n_cu*cap*4 + n_cu*80)*8 bytes): for each CU and each of its first
  * `cap` tasks, 4 uint64 words {task index << 32 | layer << 16 | type << 8 | stage,
- * begin, dependency satisfied, end} in s_memrealtime ticks (100 MHz); then
+ * begin, begin again (a task polls its inputs inside its own phases), end}
+ * in s_memrealtime ticks (100 MHz); then
  * 80 uint64 per CU: [0..2] ticks the loader waves waited for a free LDS
  * slot, [4..7] the compute waves waited for a loaded chunk, [8..11] the
  * compute waves waited in barriers, [12] compute wave 0's total time, [13]
@@ -167,8 +172,8 @@ int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t
  * last call in *status and clear them. */
 int mk_get_status(mk_handle* h, void* stream, uint32_t* status);
 
-/* Synchronise `stream` and clear all counters and status (needed after a
- * MK_STATUS_TIMEOUT). */
+/* Synchronise `stream` and clear all counters, status and the step tags of
+ * the library-owned activations (needed after a MK_STATUS_TIMEOUT). */
 int mk_reset(mk_handle* h, void* stream);
 
 /* Free library-owned memory.  The caller's weights and caches are untouched. */
