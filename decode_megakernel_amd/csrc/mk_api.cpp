@@ -62,7 +62,7 @@ struct mk_handle {
   // workspace views
   float *hres, *hmid, *ssattn, *ssmlp, *qkv, *apart, *rope, *zero;
   float *xattn, *xmlp, *attn_out, *act;
-  uint32_t *banks, *seg_ctr, *status;
+  uint32_t *banks, *status;
   int ctr_stride = 0, bank_words = 0;
   std::map<int, GraphDev> graphs;
   uint64_t step = 0;
@@ -216,14 +216,15 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   size_t o_qkv = take((size_t)L * bc * nqkv * 4);
   size_t o_aout = take((size_t)L * bc * qdim * 4);
   size_t o_act = take((size_t)L * bc * I * 4);
-  size_t o_apart = take((size_t)(h->ncu + bc * nkv) * kApartGroup * (hd + 4) * 4);
+  // attention partial slots, per layer: [L][ncu + bc*nkv][group slots][hd + 4]
+  const int G = cfg->n_q_heads / nkv, gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  size_t o_apart = take((size_t)L * (h->ncu + bc * nkv) * gm * (hd + 4) * 4);
   size_t o_banks = take((size_t)2 * h->bank_words * 4);
-  size_t o_seg = take((size_t)bc * nkv * 4);
   size_t o_status = take(64);
   size_t o_rope = take((size_t)cfg->max_seq * (hd / 2) * 2 * 4);
   size_t o_zero = take(1024);
   h->ws_bytes = off;
-  h->tagged_bytes = o_apart;  // hres .. act: the activations consumers poll by tag
+  h->tagged_bytes = o_banks;  // hres .. apart: words that carry step tags / validity flags
   if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
     delete h;
     return MK_ERR_OOM;
@@ -244,7 +245,6 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   h->act = (float*)(h->ws + o_act);
   h->apart = (float*)(h->ws + o_apart);
   h->banks = (uint32_t*)(h->ws + o_banks);
-  h->seg_ctr = (uint32_t*)(h->ws + o_seg);
   h->status = (uint32_t*)(h->ws + o_status);
   h->rope = (float*)(h->ws + o_rope);
   h->zero = (float*)(h->ws + o_zero);
@@ -412,7 +412,6 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.apart = h->apart;
   A.banks = h->banks;
   A.grp_ctr = g->d_grp;
-  A.seg_ctr = h->seg_ctr;
   A.status = h->status;
   A.rope = h->rope;
   A.zero = (const uint16_t*)h->zero;
@@ -493,7 +492,6 @@ int mk_reset(mk_handle* h, void* stream) {
   h->rowtag = 0;
   bool ok = hipMemset(h->ws, 0, h->tagged_bytes) == hipSuccess &&
             hipMemset(h->banks, 0, (size_t)2 * h->bank_words * 4) == hipSuccess &&
-            hipMemset(h->seg_ctr, 0, (size_t)h->cfg.max_batch * h->cfg.n_kv_heads * 4) == hipSuccess &&
             hipMemset(h->status, 0, 8) == hipSuccess;
   for (auto& kv : h->graphs)
     ok = ok && hipMemset(kv.second.d_grp, 0, sizeof(uint32_t) * (size_t)std::max(1, kv.second.plan.grp_counters)) == hipSuccess;

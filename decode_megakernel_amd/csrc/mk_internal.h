@@ -46,7 +46,6 @@ constexpr int kStatWords = 80;               // trace: per-CU phase totals (uint
 #define MK_PHASE_TRACE 0
 #endif
 constexpr int kCtrlBytes = MK_PHASE_TRACE ? 1536 : 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
-constexpr int kApartGroup = 8;               // group slots per attention partial
 
 enum Stage : int32_t { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_LM = 5, ST_EMBED = 6 };
 enum TaskType : int32_t { TT_EMBED = 1, TT_GEMV = 2, TT_ATTN = 3 };
@@ -140,10 +139,9 @@ struct DevArgs {
   float* attn_out;      // [L][bcap][qdim] attention output: GEMV input of O
   float* act;           // [L][bcap][I]    silu(gate) * up: GEMV input of down
   float* part;          // split-K partial blocks, 1024 floats each
-  float* apart;         // attention partials [ncu + bcap*nkv][group][hd + 4]
+  float* apart;         // attention partials [L][ncu + bcap*nkv][group slots][hd + 4]
   uint32_t* banks;      // 2 banks of kShards * ctr_stride words, then keys
   uint32_t* grp_ctr;    // split-K group counters (self-resetting)
-  uint32_t* seg_ctr;    // attention segment counters [bcap*nkv] (self-resetting)
   uint32_t* status;     // [0] status bits, [1] abort flag
   const float* rope;    // [max_seq][hd/2][2] (cos, sin)
   const uint16_t* zero; // >= 16 zero bytes: the source of masked direct-to-LDS lanes

@@ -273,6 +273,26 @@ __device__ __forceinline__ bool spin_ok(DArgs A, Ctrl* c, Spin& sp) {
   return true;
 }
 
+// The same for loops that poll data words in global memory, with their own
+// pause between polls.
+#ifndef MK_POLL_SLEEP
+#define MK_POLL_SLEEP 1
+#endif
+__device__ __forceinline__ bool poll_ok(DArgs A, Ctrl* c, Spin& sp) {
+  if (lds_aborted(c)) return false;
+  if ((++sp.it & 63) == 0) {
+    if (spin_fail(A->status, c)) return false;
+    if (now_ticks() - sp.t0 > A->timeout_ticks) {
+      atomicOr(A->status, kStatusTimeout);
+      __hip_atomic_store(A->status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&c->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return false;
+    }
+  }
+  __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
+  return true;
+}
+
 // Phase-trace accumulation into the control block (LDS): no global memory
 // operation, so the timers add no wait to the phases they time.
 __device__ __forceinline__ void trace_add(uint64_t* p, uint64_t v) { *p += v; }
@@ -856,7 +876,7 @@ __device__ __forceinline__ bool poll_ss(DArgs A, Ctrl* c, const float* ss, int n
 #pragma unroll
     for (int k = 0; k < kSsLoads; ++k) ok = ok & tag_ok(u[k], tag);
     if (__all(ok)) return true;
-    if (!spin_ok(A, c, sp)) return false;
+    if (!poll_ok(A, c, sp)) return false;
   }
 }
 
@@ -929,7 +949,7 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
         if (u < units) ok = ok & tag_ok4(va[k], tg) & tag_ok4(vb[k], tg);
       }
       if (__all(ok)) break;
-      if (!spin_ok(A, c, sp)) return false;
+      if (!poll_ok(A, c, sp)) return false;
     }
 #pragma unroll
     for (int k = 0; k < kStageBatch; ++k) {
@@ -1312,7 +1332,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
             ok = ok & tag_ok(__float_as_uint(resid[i][j]), (tags >> n) & 1u);
         }
       if (__all(ok)) break;
-      if (!spin_ok(A, c, sp)) return false;
+      if (!poll_ok(A, c, sp)) return false;
 #pragma unroll
       for (int i = 0; i < kResidTiles; ++i)
 #pragma unroll
@@ -1506,7 +1526,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
             if (need) ok = ok & tag_ok(__float_as_uint(rs[j]), (tags >> n) & 1u);
           }
           if (__all(ok)) break;
-          if (!spin_ok(A, c, sp)) return false;
+          if (!poll_ok(A, c, sp)) return false;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) rs[j] = untagf(rs[j]);
@@ -1685,38 +1705,75 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   auto bcast = [](float v, int src_lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
   };
-  // the finisher: compute wave w merges heads w, w + 4 of a segment from
-  // its pieces' partials; LPP lanes cover one piece's head vector, PPI
-  // pieces per pass; all loads of a batch are issued before any is used
+  // The finisher of a segment split over several CUs is the CU holding its
+  // first rows.  Pieces publish their partials (o, m, l per head) into
+  // per-layer slots with the lowest mantissa bit of every word set; the
+  // finisher polls the slots until every word is set, merges, stores the
+  // output and clears the slots (it is their only reader, and the next write
+  // of a slot is in a later step).  Compute wave w merges heads w, w + 4;
+  // LPP lanes cover one piece's head vector, PPI pieces per pass; all loads
+  // of a pass are issued before any is used.
   struct Pend {
     int sid, npieces, c_first, i, g;
     long long seg_start;
   };
   const int pstride = GM * SW;
-  auto finish_segment = [&](const Pend& pd) {
+  float* const apart_l = A->apart + (size_t)l * (A->ncu + A->bcap * A->nkv) * pstride;
+  auto finish_segment = [&](const Pend& pd) -> bool {
     const int sid = pd.sid, npieces = pd.npieces, c_first = pd.c_first;
     const long long seg_start = pd.seg_start;
     float* ob = A->attn_out + ((size_t)l * A->bcap + pd.i) * A->qdim + (size_t)pd.g * G * HD;
     constexpr int LPP = HD / 4, PPI = 64 / LPP, kMergeIt = 16;
     const int sub = lane / LPP, el = (lane % LPP) * 4;
-    auto piece_src = [&](int pc) -> const float* {
+    // byte offset of piece pc's record from the layer's (wave-uniform) slot
+    // base: per-lane offsets keep every access a single buffer instruction
+    auto piece_off = [&](int pc) -> uint32_t {
       const int pcu = W >= nacu ? c_first + pc : cu_of(seg_start + pc, W, nacu);
-      return A->apart + (size_t)(pcu + sid) * pstride;
+      return (uint32_t)(pcu + sid) * (uint32_t)(pstride * 4);
     };
     for (int h = w; h < G; h += kComputeWaves) {
       float Mrun = -INFINITY, Lrun = 0.f;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int p0 = 0; p0 < npieces; p0 += PPI * kMergeIt) {
         u32x4 ov[kMergeIt];
+        u32x2 ml[kMergeIt];
+        uint32_t po[kMergeIt];
+#pragma unroll
+        for (int k = 0; k < kMergeIt; ++k) {
+          const int pc = p0 + k * PPI + sub;
+          po[k] = piece_off(pc < npieces ? pc : 0);
+        }
+        Spin sp = spin_start();
+        const uint64_t tp0 = MK_PHASE_TRACE && ast ? now_ticks() : 0;
+        for (;;) {
+          if (MK_PHASE_TRACE && ast) trace_add(MK_PSTAT(c, 46), 1);
+          // every load of the pass in flight before any flag is tested
+#pragma unroll
+          for (int k = 0; k < kMergeIt; ++k) {
+            ov[k] = co_load16(apart_l, po[k] + (uint32_t)((h * SW + el) * 4));
+            ml[k] = co_load8(apart_l, po[k] + (uint32_t)((h * SW + HD) * 4));
+          }
+          uint32_t flags = 1u;
+#pragma unroll
+          for (int k = 0; k < kMergeIt; ++k) {
+            const uint32_t f = ov[k].x & ov[k].y & ov[k].z & ov[k].w & ml[k].x & ml[k].y;
+            flags &= p0 + k * PPI + sub < npieces ? f : 1u;
+          }
+          if (__all((flags & 1u) != 0)) break;
+          if (!poll_ok(A, c, sp)) return false;
+        }
+        if (MK_PHASE_TRACE && ast) trace_add(MK_PSTAT(c, 47), now_ticks() - tp0);
         float m2[kMergeIt], l2[kMergeIt];
 #pragma unroll
         for (int k = 0; k < kMergeIt; ++k) {
           const int pc = p0 + k * PPI + sub;
-          const float* src = piece_src(pc < npieces ? pc : 0);
-          ov[k] = co_load16(src, (uint32_t)((h * SW + el) * 4));
-          const u32x2 ml = co_load8(src, (uint32_t)((h * SW + HD) * 4));
-          m2[k] = pc < npieces ? __uint_as_float(ml.x) : -INFINITY;
-          l2[k] = __uint_as_float(ml.y);
+          if (pc < npieces) {
+            co_store16(apart_l, po[k] + (uint32_t)((h * SW + el) * 4), u32x4{0u, 0u, 0u, 0u});
+            if (el == 0) co_store8(apart_l, po[k] + (uint32_t)((h * SW + HD) * 4), u32x2{0u, 0u});
+          }
+          ov[k] = untag4(ov[k]);
+          m2[k] = pc < npieces ? __uint_as_float(untag(ml[k].x)) : -INFINITY;
+          l2[k] = __uint_as_float(untag(ml[k].y));
         }
         float mb = -INFINITY;
 #pragma unroll
@@ -1755,7 +1812,10 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       }
     }
     if (ast) trace_add(ast + 8, 1);
+    return true;
   };
+  Pend pend{};
+  bool has_pend = false;
   // analysis builds: sub-phases of the query preparation (compute wave 0)
   uint64_t* qsp = ast ? MK_PSTAT(c, 32) : nullptr;
   uint64_t tq = qsp ? now_ticks() : 0;
@@ -1823,7 +1883,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
           const bool ok = !valid || (tag_ok4(a0, tg) & tag_ok4(a1, tg) & tag_ok4(b0, tg) & tag_ok4(b1, tg) &
                                      (!is_k || (tag_ok4(v0, tg) & tag_ok4(v1, tg))));
           if (__all(ok)) break;
-          if (!spin_ok(A, c, sp)) return false;
+          if (!poll_ok(A, c, sp)) return false;
         }
         a0 = untag4(a0);
         a1 = untag4(a1);
@@ -2071,7 +2131,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     const int npieces = W >= nacu ? c_last - c_first + 1
                                    : (int)(cu_lo(c_last + 1, W, nacu) - cu_lo(c_first, W, nacu));
     float* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
-    float* dst = A->apart + (size_t)(cu + P.sid) * pstride;
+    float* dst = apart_l + (size_t)(cu + P.sid) * pstride;
     // merge the four wave states: wave w takes heads w, w + 4; each lane HD/64 dims
     constexpr int DPL = HD / 64;
     const float* s0 = stb + (pidx & 1) * stride_st;
@@ -2098,34 +2158,27 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         if constexpr (DPL == 2) co_store8(ob, (uint32_t)((h * HD + 2 * lane) * 4), u32x2{tagged(O[0] * inv, tg), tagged(O[1] * inv, tg)});
         else co_store_tag(ob, (uint32_t)((h * HD + lane) * 4), O[0] * inv, tg);
       } else {
-        if constexpr (DPL == 2) co_store8(dst, (uint32_t)((h * SW + 2 * lane) * 4), u32x2{__float_as_uint(O[0]), __float_as_uint(O[1])});
-        else co_storef(dst, (uint32_t)((h * SW + lane) * 4), O[0]);
-        if (lane == 0) co_store8(dst, (uint32_t)((h * SW + HD) * 4), u32x2{__float_as_uint(M), __float_as_uint(L)});
+        // every word with its lowest bit set: the finisher's validity flag
+        if constexpr (DPL == 2) co_store8(dst, (uint32_t)((h * SW + 2 * lane) * 4), u32x2{tagged(O[0], 1u), tagged(O[1], 1u)});
+        else co_store_tag(dst, (uint32_t)((h * SW + lane) * 4), O[0], 1u);
+        if (lane == 0) co_store8(dst, (uint32_t)((h * SW + HD) * 4), u32x2{tagged(M, 1u), tagged(L, 1u)});
       }
     }
     mark(3);
-    if (npieces > 1) {
-      // the last piece of the segment to arrive merges it
-      wait_mem();
-      if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
-      if (w == 0) {
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(A->seg_ctr + P.sid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __shfl(old, 0);
-        const int fin = (int)old == npieces - 1;
-        if (fin && lane == 0) __hip_atomic_store(A->seg_ctr + P.sid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) lds_st_rel(&c->fin, fin);
-      }
-      if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
-      if (lds_ld_acq(&c->fin)) {
-        finish_segment(Pend{P.sid, npieces, c_first, P.i, P.g, P.seg_start});
-        mark(4);
-      }
+    // a segment continued on other CUs is finished here once this CU's
+    // pieces are done (only the last piece of a CU's range can be one)
+    if (npieces > 1 && cu == c_first) {
+      pend = Pend{P.sid, npieces, c_first, P.i, P.g, P.seg_start};
+      has_pend = true;
     }
     mark(5);
     qc += P.nch;
     ++pidx;
     }
+  }
+  if (has_pend) {
+    if (!finish_segment(pend)) return false;
+    mark(4);
   }
   // the O projection polls the tagged outputs: no completion wait, no counter
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
