@@ -116,6 +116,7 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
   p.xb_bytes = xb;
   p.mfma_min_batch = mfma_min;
   p.gemv_mode = env_int("MK_GEMV_MODE", 0);
+  p.skip_prev = env_int("MK_PLAN_SKIP_PREV", 2);
   return p;
 }
 

@@ -168,6 +168,8 @@ struct PlanCfg {
   int xb_bytes;         // LDS bytes available to stage a GEMV input slice
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
   int gemv_mode = 0;    // 0: cheaper of row-owner / stream-K per stage, 1: row-owner, 2: stream-K
+  int skip_prev = 2;    // row-owner stages skip the CUs of a previous stage that left CUs idle
+                        // when the tiles per CU grow by at most skip_prev - 1 (0: never)
 };
 constexpr int kTaskSignal = 1;
 

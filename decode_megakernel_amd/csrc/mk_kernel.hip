@@ -220,6 +220,8 @@ struct Ctrl {
   float rms[kMaxBatch];
 #if MK_PHASE_TRACE
   uint64_t pstat[48];  // phase timers of compute wave 0, flushed at the end
+  uint64_t ppack;      // the current task's phase offsets (analysis trace word 2)
+  uint32_t npoll;      // polls of the current task's inputs (compute wave 0)
 #endif
 };
 
@@ -233,8 +235,27 @@ __device__ __forceinline__ char* xb_stage(DArgs A) { return mk_lds + (size_t)A->
 __device__ __forceinline__ float* red_scratch(DArgs A) { return (float*)(xb_stage(A) + A->xb_bytes); }
 __device__ __forceinline__ Ctrl* ctrl_block(DArgs A) { return (Ctrl*)((char*)red_scratch(A) + kRedBytes); }
 
-__device__ __forceinline__ int lds_ld_acq(int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-__device__ __forceinline__ void lds_st_rel(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+// Flags that order LDS accesses between the waves of one CU.  They use LDS
+// instructions with an LDS-only wait (lgkmcnt): an acquire or release atomic
+// at workgroup scope would also wait for every global load and store the wave
+// has in flight (gfx9 counts both in vmcnt), which puts the completion of
+// epilogue stores on the path of every barrier.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// read a flag; LDS reads issued after it see what was written before it was set
+__device__ __forceinline__ int lds_ld_acq(int* p) {
+  int v;
+  __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+// set a flag once this wave's earlier LDS accesses are complete
+__device__ __forceinline__ void lds_st_rel(int* p, int v) {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_add_rel(int* p, int v) {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\tds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
 __device__ __forceinline__ bool lds_aborted(Ctrl* c) { return __hip_atomic_load(&c->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0; }
 
 __device__ __forceinline__ bool global_aborted(DArgs A) {
@@ -317,7 +338,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Software barrier among the compute waves (the loader waves never join).
 __device__ __forceinline__ bool cbar(DArgs A, Ctrl* c, int& gen, int lane, uint64_t* wait_ticks = nullptr) {
   ++gen;
-  if (lane == 0) __hip_atomic_fetch_add(&c->bar, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0) lds_add_rel(&c->bar, 1);
   const int target = gen * kComputeWaves;
   if (lds_ld_acq(&c->bar) >= target) return true;
   Spin sp = spin_start();
@@ -525,9 +546,6 @@ __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rp
 // writes go through inline LDS instructions with explicit waits: the
 // compiler cannot tell a flag from the ring that the DMA writes, and would
 // otherwise drain every outstanding load before each flag access.
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
 __device__ __forceinline__ int lds_flag_read(const int* p) {
   int v;
   __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
@@ -930,6 +948,9 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
     u32x4 va[kStageBatch], vb[kStageBatch];
     Spin sp = spin_start();
     for (;;) {
+#if MK_PHASE_TRACE
+      if (A->trace && w == 0 && lane == 0) c->npoll += 1;
+#endif
       bool ok = true;
 #pragma unroll
       for (int k = 0; k < kStageBatch; ++k) {
@@ -1244,11 +1265,15 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
                       ? MK_PSTAT(c, 10 + 4 * (t.stage == ST_LM ? 1 : t.stage))
                       : nullptr;
   uint64_t gt = gst ? now_ticks() : 0;
+  const uint64_t gt0 = gt;
+  uint64_t gpack = 0;
   auto gmark = [&](int k) {
     if (gst) {
       const uint64_t tn = now_ticks();
       trace_add(gst + k, tn - gt);
       gt = tn;
+      // per-task offsets of the first staging, the chunks and the epilogue
+      if (k < 3 && !((gpack >> (16 * k)) & 0xFFFF)) gpack |= ((tn - gt0) & 0xFFFF) << (16 * k);
     }
   };
   float vacc[TPW][16][NV];
@@ -1569,6 +1594,12 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     }
   }
   gmark(3);
+#if MK_PHASE_TRACE
+  if (gst) {
+    c->ppack = gpack | ((uint64_t)(c->npoll & 0xFFFF) << 48);
+    c->npoll = 0;
+  }
+#endif
   if (A->trace) s.t_epi += now_ticks() - te0;
   return true;
 }
@@ -1695,6 +1726,12 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   // trace: attention phase totals of compute wave 0 (per-CU stats words 32..41)
   uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0) ? MK_PSTAT(c, 0) : nullptr;
   uint64_t tlast = ast ? now_ticks() : 0;
+  // per-task offsets (analysis trace word 2): queries ready, pieces done, finish done
+  const uint64_t at0 = tlast;
+  uint64_t apack = 0;
+  auto amark = [&](int k) {
+    if (ast && !((apack >> (16 * k)) & 0xFFFF)) apack |= ((now_ticks() - at0) & 0xFFFF) << (16 * k);
+  };
   auto mark = [&](int k) {
     if (ast) {
       const uint64_t tn = now_ticks();
@@ -1747,6 +1784,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         const uint64_t tp0 = MK_PHASE_TRACE && ast ? now_ticks() : 0;
         for (;;) {
           if (MK_PHASE_TRACE && ast) trace_add(MK_PSTAT(c, 46), 1);
+#if MK_PHASE_TRACE
+          if (ast) c->npoll += 1;
+#endif
           // every load of the pass in flight before any flag is tested
 #pragma unroll
           for (int k = 0; k < kMergeIt; ++k) {
@@ -1922,6 +1962,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     qmark(2);
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     qmark(3);
+    amark(0);
     for (int bk = 0; bk < nbp; ++bk) {
     next_piece(c, A->b, A->nkv, RPC, bpos, hi, P);
     if (ast) trace_add(ast + 7, 1);
@@ -2176,14 +2217,20 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     ++pidx;
     }
   }
+  amark(1);
   if (has_pend) {
     if (!finish_segment(pend)) return false;
     mark(4);
   }
+  amark(2);
   // the O projection polls the tagged outputs: no completion wait, no counter
   if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
   s.synced = 1;
   mark(6);
+#if MK_PHASE_TRACE
+  if (ast) c->ppack = apack | ((uint64_t)(c->npoll & 0xFFFF) << 48);
+  if (ast) c->npoll = 0;
+#endif
   s.x_stage = -1;  // the staging buffer held softmax states
   return true;
 }
@@ -2247,7 +2294,12 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
     if (tr && ti < A->trace_cap) {
       tr[ti * 4 + 0] = ((uint64_t)ti << 32) | ((uint64_t)(t.layer & 0xFFFF) << 16) | ((uint64_t)t.type << 8) | (uint64_t)t.stage;
       tr[ti * 4 + 1] = t_begin;
+#if MK_PHASE_TRACE
+      tr[ti * 4 + 2] = c->ppack;
+      c->ppack = 0;
+#else
       tr[ti * 4 + 2] = t_dep;
+#endif
       tr[ti * 4 + 3] = now_ticks();
     }
   }
@@ -2300,6 +2352,10 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
   if (tid < kMaxBatch) c->lmkey[tid] = 0ull;
 #if MK_PHASE_TRACE
   if (tid < 48) c->pstat[tid] = 0;
+  if (tid == 0) {
+    c->ppack = 0;
+    c->npoll = 0;
+  }
 #endif
   if (tid == 0) {
     c->dep = 0;

@@ -226,14 +226,35 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
       }
   }
 
+  // CUs that ran a task of the stage emitted last: a stage that left some CUs
+  // idle finishes on the others, so the next row-owner stage avoids them
+  // (its tasks then wait for their inputs on CUs that are already free)
+  // unless that raises its tiles per CU by skip_prev or more.
+  std::vector<char> prev_used(ncu, 1);
   auto emit_gemv = [&](int st, int layer, int wait, int signal) {
     const int M = stage_rows(pc, st), K = stage_k(pc, st);
     const Tiling& T = tl[st];
     const int nst = (M + 15) / 16;
     if (T.owner) {
-      for (int c = 0; c < ncu; ++c) {
-        const int t0 = (int)((long long)nst * c / ncu), t1 = (int)((long long)nst * (c + 1) / ncu);
+      std::vector<int> cus;
+      int nprev = 0;
+      for (int c = 0; c < ncu; ++c) nprev += prev_used[c];
+      if (pc.skip_prev > 0 && nprev < ncu) {
+        const int nfree = ncu - nprev;
+        const int per_all = (nst + ncu - 1) / ncu, per_free = (nst + nfree - 1) / nfree;
+        if (per_free - per_all < pc.skip_prev)
+          for (int c = 0; c < ncu; ++c)
+            if (!prev_used[c]) cus.push_back(c);
+      }
+      if (cus.empty())
+        for (int c = 0; c < ncu; ++c) cus.push_back(c);
+      const int nc = (int)cus.size();
+      std::fill(prev_used.begin(), prev_used.end(), 0);
+      for (int ci = 0; ci < nc; ++ci) {
+        const int c = cus[ci];
+        const int t0 = (int)((long long)nst * ci / nc), t1 = (int)((long long)nst * (ci + 1) / nc);
         if (t1 <= t0) continue;
+        prev_used[c] = 1;
         const int n = t1 - t0, ntask = (n + T.tmax - 1) / T.tmax;
         for (int k = 0; k < ntask; ++k) {
           const int a = t0 + n * k / ntask, e = t0 + n * (k + 1) / ntask;
@@ -253,6 +274,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
       return;
     }
     std::vector<int> seen(T.ngroups, 0);
+    std::fill(prev_used.begin(), prev_used.end(), 1);
     for (int c = 0; c < ncu; ++c) {
       long long c0 = T.ncols * c / ncu, c1 = T.ncols * (c + 1) / ncu;
       int first = (int)S[c].size();
@@ -285,6 +307,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   for (int l = 0; l < pc.L; ++l) {
     int wait_in = l == 0 ? ctr_embed() : ctr_stage(l - 1, ST_DOWN);
     emit_gemv(ST_QKV, l, wait_in, ctr_stage(l, ST_QKV));
+    std::fill(prev_used.begin(), prev_used.end(), 1);  // attention spreads over every CU
     for (int c = 0; c < ncu; ++c) {
       Task t = base_task(TT_ATTN, ST_ATTN, l);
       t.wait_ctr = ctr_stage(l, ST_QKV);
