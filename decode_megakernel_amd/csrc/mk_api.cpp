@@ -29,6 +29,7 @@ struct GraphDev {
   Task* d_tasks = nullptr;
   int* d_off = nullptr;
   int* d_expect = nullptr;
+  int* d_attn_map = nullptr;
   float* d_part = nullptr;
   uint32_t* d_grp = nullptr;
 };
@@ -117,6 +118,7 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
   p.mfma_min_batch = mfma_min;
   p.gemv_mode = env_int("MK_GEMV_MODE", 0);
   p.skip_prev = env_int("MK_PLAN_SKIP_PREV", 2);
+  p.attn_idle = env_int("MK_ATTN_IDLE", 1);
   return p;
 }
 
@@ -314,6 +316,7 @@ static void free_graph(GraphDev& g) {
   (void)hipFree(g.d_tasks);
   (void)hipFree(g.d_off);
   (void)hipFree(g.d_expect);
+  (void)hipFree(g.d_attn_map);
   (void)hipFree(g.d_part);
   (void)hipFree(g.d_grp);
   free_plan(&g.plan);
@@ -333,6 +336,7 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
   bool ok = hipMalloc(&g.d_tasks, sizeof(Task) * (size_t)std::max(1, P.n_tasks)) == hipSuccess &&
             hipMalloc(&g.d_off, sizeof(int) * (h->ncu + 1)) == hipSuccess &&
             hipMalloc(&g.d_expect, sizeof(int) * (size_t)P.n_counters * kShards) == hipSuccess &&
+            hipMalloc(&g.d_attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1)) == hipSuccess &&
             hipMalloc(&g.d_part, sizeof(float) * 1024 * (size_t)std::max(1, P.part_blocks)) == hipSuccess &&
             hipMalloc(&g.d_grp, sizeof(uint32_t) * (size_t)std::max(1, P.grp_counters)) == hipSuccess;
   if (!ok) {
@@ -342,6 +346,7 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
   ok = hipMemcpy(g.d_tasks, P.tasks, sizeof(Task) * P.n_tasks, hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(g.d_off, P.task_off, sizeof(int) * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(g.d_expect, P.expect, sizeof(int) * (size_t)P.n_counters * kShards, hipMemcpyHostToDevice) == hipSuccess &&
+       hipMemcpy(g.d_attn_map, P.attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemset(g.d_grp, 0, sizeof(uint32_t) * (size_t)std::max(1, P.grp_counters)) == hipSuccess;
   if (!ok) {
     free_graph(g);
@@ -419,6 +424,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.tasks = g->d_tasks;
   A.task_off = g->d_off;
   A.expect = g->d_expect;
+  A.attn_map = g->d_attn_map;
   A.ctr_stride = h->ctr_stride;
   A.bank_words = h->bank_words;
   for (int i = 0; i < 6; ++i) A.grp_off[i] = g->plan.grp_off[i];

@@ -149,6 +149,7 @@ struct DevArgs {
   const Task* tasks;
   const int32_t* task_off;  // [ncu + 1]
   const int32_t* expect;    // [n_counters][kShards]
+  const int32_t* attn_map;  // per layer [ncu + 1]: attention slot of each CU, then the slot cap (0: none)
   int32_t ctr_stride;
   int32_t bank_words;       // words per bank (counters + keys)
   int32_t grp_off[6];       // per-stage base into grp_ctr
@@ -168,6 +169,7 @@ struct PlanCfg {
   int xb_bytes;         // LDS bytes available to stage a GEMV input slice
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
   int gemv_mode = 0;    // 0: cheaper of row-owner / stream-K per stage, 1: row-owner, 2: stream-K
+  int attn_idle = 1;    // attention prefers the CUs its layer's QKV stage left idle
   int skip_prev = 2;    // row-owner stages skip the CUs of a previous stage that left CUs idle
                         // when the tiles per CU grow by at most skip_prev - 1 (0: never)
 };
@@ -193,6 +195,7 @@ struct Plan {
   Task* tasks = nullptr;     // host copy, n_tasks
   int* task_off = nullptr;   // ncu + 1
   int* expect = nullptr;     // n_counters * kShards
+  int* attn_map = nullptr;   // L * (ncu + 1): attention slot per CU, then the slot cap
 };
 
 // Builds and validates the per-CU streams; returns 0 or an MK_ERR_* code.

@@ -509,6 +509,19 @@ __device__ __forceinline__ int attn_ncu(long long W, int ncu) {
   const long long n = (W + kAttnMinRows - 1) / kAttnMinRows;
   return n < 1 ? 1 : (n > ncu ? ncu : (int)n);
 }
+// Attention works in CU slots: the schedule numbers first the CUs its layer's
+// QKV stage left idle (they are already waiting, cached rows loaded), and the
+// rows go to those alone when that keeps every CU at or under kAttnCapRows.
+constexpr int kAttnCapRows = 256;
+__device__ __forceinline__ int attn_slot(DArgs A, int l, int cu) {
+  return as_const(A->attn_map)[(size_t)l * (A->ncu + 1) + cu];
+}
+__device__ __forceinline__ int attn_nacu(DArgs A, int l, long long W) {
+  int n = attn_ncu(W, A->ncu);
+  const int cap = as_const(A->attn_map)[(size_t)l * (A->ncu + 1) + A->ncu];
+  if (cap > 0 && n > cap && (W + cap - 1) / cap <= kAttnCapRows) n = cap;
+  return n;
+}
 
 __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rpc, long long& pos, long long hi, Piece& P) {
   if (pos >= hi) return false;
@@ -747,9 +760,9 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
       qbase += nch;
     } else if (t.type == TT_ATTN) {
       const long long W = attn_total_r(sl, A->b, A->nkv);
-      const int nacu = attn_ncu(W, A->ncu);
-      long long pos = cu < nacu ? cu_lo(cu, W, nacu) : W;
-      const long long hi = cu < nacu ? cu_lo(cu + 1, W, nacu) : W;
+      const int nacu = attn_nacu(A, t.layer, W), slot = attn_slot(A, t.layer, cu);
+      long long pos = slot < nacu ? cu_lo(slot, W, nacu) : W;
+      const long long hi = slot < nacu ? cu_lo(slot + 1, W, nacu) : W;
       Piece P;
       int pbase = qbase;
       while (next_piece_r(sl, A->b, A->nkv, rpc, pos, hi, P)) {
@@ -780,12 +793,12 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
 }
 
 // ================================================================ compute
-__device__ __forceinline__ int attn_task_chunks(DArgs A, int cu, int rpc) {
+__device__ __forceinline__ int attn_task_chunks(DArgs A, int cu, int l, int rpc) {
   A = uni(A);
   const Ctrl* c = ctrl_block(A);
   long long W = attn_total(c, A->b, A->nkv);
-  const int nacu = attn_ncu(W, A->ncu);
-  long long pos = cu < nacu ? cu_lo(cu, W, nacu) : W, hi = cu < nacu ? cu_lo(cu + 1, W, nacu) : W;
+  const int nacu = attn_nacu(A, l, W), slot = attn_slot(A, l, cu);
+  long long pos = slot < nacu ? cu_lo(slot, W, nacu) : W, hi = slot < nacu ? cu_lo(slot + 1, W, nacu) : W;
   Piece P;
   int n = 0;
   while (next_piece(c, A->b, A->nkv, rpc, pos, hi, P)) n += P.nch;
@@ -1707,8 +1720,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   const int r16 = lane & 15, lr = lane >> 4;  // MFMA output layout: row r16 of a block, heads 4 lr + i
   const float qscale = kLog2e / sqrtf((float)HD);
   const long long W = attn_total(c, A->b, A->nkv);
-  const int nacu = attn_ncu(W, A->ncu);
-  long long pos = cu < nacu ? cu_lo(cu, W, nacu) : W, hi = cu < nacu ? cu_lo(cu + 1, W, nacu) : W;
+  // this CU's slot: pieces, partial slots and the finisher role go by slot
+  const int nacu = attn_nacu(A, t.layer, W), slot = attn_slot(A, t.layer, cu);
+  long long pos = slot < nacu ? cu_lo(slot, W, nacu) : W, hi = slot < nacu ? cu_lo(slot + 1, W, nacu) : W;
   Piece P;
   int qc = s.q, pidx = 0;
   const MK_AS4 LayerW& lw = as_const(A->layers)[l];
@@ -2172,7 +2186,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     const int npieces = W >= nacu ? c_last - c_first + 1
                                    : (int)(cu_lo(c_last + 1, W, nacu) - cu_lo(c_first, W, nacu));
     float* ob = A->attn_out + ((size_t)l * A->bcap + P.i) * A->qdim + (size_t)P.g * G * HD;
-    float* dst = apart_l + (size_t)(cu + P.sid) * pstride;
+    float* dst = apart_l + (size_t)(slot + P.sid) * pstride;
     // merge the four wave states: wave w takes heads w, w + 4; each lane HD/64 dims
     constexpr int DPL = HD / 64;
     const float* s0 = stb + (pidx & 1) * stride_st;
@@ -2208,7 +2222,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     mark(3);
     // a segment continued on other CUs is finished here once this CU's
     // pieces are done (only the last piece of a CU's range can be one)
-    if (npieces > 1 && cu == c_first) {
+    if (npieces > 1 && slot == c_first) {
       pend = Pend{P.sid, npieces, c_first, P.i, P.g, P.seg_start};
       has_pend = true;
     }
@@ -2285,7 +2299,7 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
       had_lm = had_lm || t.stage == ST_LM;
     } else if (t.type == TT_ATTN) {
       ok = A->hd == 128 ? attn_dispatch<128>(A, T + ti, cu, w, lane) : attn_dispatch<64>(A, T + ti, cu, w, lane);
-      nch = attn_task_chunks(A, cu, rpc);
+      nch = attn_task_chunks(A, cu, t.layer, rpc);
     } else {
       ok = embed_task(A, T + ti, cu, w, lane);
     }

@@ -119,6 +119,8 @@ void free_plan(Plan* p) {
   free(p->tasks);
   free(p->task_off);
   free(p->expect);
+  free(p->attn_map);
+  p->attn_map = nullptr;
   p->tasks = nullptr;
   p->task_off = nullptr;
   p->expect = nullptr;
@@ -231,6 +233,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   // (its tasks then wait for their inputs on CUs that are already free)
   // unless that raises its tiles per CU by skip_prev or more.
   std::vector<char> prev_used(ncu, 1);
+  std::vector<int> attn_map((size_t)pc.L * (ncu + 1), 0);
   auto emit_gemv = [&](int st, int layer, int wait, int signal) {
     const int M = stage_rows(pc, st), K = stage_k(pc, st);
     const Tiling& T = tl[st];
@@ -307,7 +310,24 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   for (int l = 0; l < pc.L; ++l) {
     int wait_in = l == 0 ? ctr_embed() : ctr_stage(l - 1, ST_DOWN);
     emit_gemv(ST_QKV, l, wait_in, ctr_stage(l, ST_QKV));
-    std::fill(prev_used.begin(), prev_used.end(), 1);  // attention spreads over every CU
+    // attention slots: the CUs this layer's QKV stage left idle come first
+    // (they wait for q/k/v with their cached rows already loaded); the
+    // device caps the CUs at the idle ones when that keeps pieces short
+    {
+      int* m = &attn_map[(size_t)l * (ncu + 1)];
+      int k = 0, nidle = 0;
+      for (int c = 0; c < ncu; ++c)
+        if (!prev_used[c]) m[c] = k++;
+      nidle = k;
+      for (int c = 0; c < ncu; ++c)
+        if (prev_used[c]) m[c] = k++;
+      m[ncu] = (pc.attn_idle && nidle >= ncu / 8 && nidle < ncu) ? nidle : 0;
+      // the next stage treats the CUs attention runs on as the busy ones
+      if (m[ncu] > 0)
+        for (int c = 0; c < ncu; ++c) prev_used[c] = !prev_used[c];
+      else
+        std::fill(prev_used.begin(), prev_used.end(), 1);
+    }
     for (int c = 0; c < ncu; ++c) {
       Task t = base_task(TT_ATTN, ST_ATTN, l);
       t.wait_ctr = ctr_stage(l, ST_QKV);
@@ -430,7 +450,8 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   P.tasks = (Task*)malloc(sizeof(Task) * (size_t)std::max(1, n_tasks));
   P.task_off = (int*)malloc(sizeof(int) * (size_t)(ncu + 1));
   P.expect = (int*)malloc(sizeof(int) * expect.size());
-  if (!P.tasks || !P.task_off || !P.expect) {
+  P.attn_map = (int*)malloc(sizeof(int) * attn_map.size());
+  if (!P.tasks || !P.task_off || !P.expect || !P.attn_map) {
     free_plan(&P);
     return MK_ERR_OOM;
   }
@@ -441,6 +462,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   }
   P.task_off[ncu] = k;
   memcpy(P.expect, expect.data(), sizeof(int) * expect.size());
+  memcpy(P.attn_map, attn_map.data(), sizeof(int) * attn_map.size());
   *out = P;
   return MK_OK;
 }
