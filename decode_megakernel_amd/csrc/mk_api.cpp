@@ -31,7 +31,6 @@ struct GraphDev {
   int* d_expect = nullptr;
   int* d_attn_map = nullptr;
   float* d_part = nullptr;
-  uint32_t* d_grp = nullptr;
 };
 
 int env_int(const char* name, int def) {
@@ -318,7 +317,6 @@ static void free_graph(GraphDev& g) {
   (void)hipFree(g.d_expect);
   (void)hipFree(g.d_attn_map);
   (void)hipFree(g.d_part);
-  (void)hipFree(g.d_grp);
   free_plan(&g.plan);
 }
 
@@ -337,8 +335,7 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
             hipMalloc(&g.d_off, sizeof(int) * (h->ncu + 1)) == hipSuccess &&
             hipMalloc(&g.d_expect, sizeof(int) * (size_t)P.n_counters * kShards) == hipSuccess &&
             hipMalloc(&g.d_attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1)) == hipSuccess &&
-            hipMalloc(&g.d_part, sizeof(float) * 1024 * (size_t)std::max(1, P.part_blocks)) == hipSuccess &&
-            hipMalloc(&g.d_grp, sizeof(uint32_t) * (size_t)std::max(1, P.grp_counters)) == hipSuccess;
+            hipMalloc(&g.d_part, sizeof(float) * 1024 * (size_t)(pc.L + 1) * std::max(1, P.part_blocks)) == hipSuccess;
   if (!ok) {
     free_graph(g);
     return MK_ERR_OOM;
@@ -347,7 +344,7 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
        hipMemcpy(g.d_off, P.task_off, sizeof(int) * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(g.d_expect, P.expect, sizeof(int) * (size_t)P.n_counters * kShards, hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(g.d_attn_map, P.attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemset(g.d_grp, 0, sizeof(uint32_t) * (size_t)std::max(1, P.grp_counters)) == hipSuccess;
+       hipMemset(g.d_part, 0, sizeof(float) * 1024 * (size_t)(pc.L + 1) * std::max(1, P.part_blocks)) == hipSuccess;
   if (!ok) {
     free_graph(g);
     return MK_ERR_HIP;
@@ -417,7 +414,6 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.part = g->d_part;
   A.apart = h->apart;
   A.banks = h->banks;
-  A.grp_ctr = g->d_grp;
   A.status = h->status;
   A.rope = h->rope;
   A.zero = (const uint16_t*)h->zero;
@@ -427,7 +423,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.attn_map = g->d_attn_map;
   A.ctr_stride = h->ctr_stride;
   A.bank_words = h->bank_words;
-  for (int i = 0; i < 6; ++i) A.grp_off[i] = g->plan.grp_off[i];
+  A.part_blocks = std::max(1, g->plan.part_blocks);
   A.ncu = h->ncu;
   A.nslot = h->nslot;
   A.xb_bytes = h->xb;
@@ -501,7 +497,8 @@ int mk_reset(mk_handle* h, void* stream) {
             hipMemset(h->banks, 0, (size_t)2 * h->bank_words * 4) == hipSuccess &&
             hipMemset(h->status, 0, 8) == hipSuccess;
   for (auto& kv : h->graphs)
-    ok = ok && hipMemset(kv.second.d_grp, 0, sizeof(uint32_t) * (size_t)std::max(1, kv.second.plan.grp_counters)) == hipSuccess;
+    ok = ok && hipMemset(kv.second.d_part, 0,
+                         sizeof(float) * 1024 * (size_t)(h->cfg.n_layers + 1) * std::max(1, kv.second.plan.part_blocks)) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   return ok ? MK_OK : MK_ERR_HIP;
 }

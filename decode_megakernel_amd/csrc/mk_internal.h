@@ -138,10 +138,9 @@ struct DevArgs {
   float* qkv;           // [L][bcap][nqkv]
   float* attn_out;      // [L][bcap][qdim] attention output: GEMV input of O
   float* act;           // [L][bcap][I]    silu(gate) * up: GEMV input of down
-  float* part;          // split-K partial blocks, 1024 floats each
+  float* part;          // split-K partial blocks, [L + 1 (LM head)][part_blocks][1024 floats]
   float* apart;         // attention partials [L][ncu + bcap*nkv][group slots][hd + 4]
   uint32_t* banks;      // 2 banks of kShards * ctr_stride words, then keys
-  uint32_t* grp_ctr;    // split-K group counters (self-resetting)
   uint32_t* status;     // [0] status bits, [1] abort flag
   const float* rope;    // [max_seq][hd/2][2] (cos, sin)
   const uint16_t* zero; // >= 16 zero bytes: the source of masked direct-to-LDS lanes
@@ -152,7 +151,7 @@ struct DevArgs {
   const int32_t* attn_map;  // per layer [ncu + 1]: attention slot of each CU, then the slot cap (0: none)
   int32_t ctr_stride;
   int32_t bank_words;       // words per bank (counters + keys)
-  int32_t grp_off[6];       // per-stage base into grp_ctr
+  int32_t part_blocks;      // split-K partial blocks per layer
   int32_t ncu;
   int32_t nslot;
   int32_t xb_bytes;

@@ -1473,54 +1473,55 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   };
   const int nepi = lead ? nown : 0;  // owned sub-tiles whose epilogue this wave runs
   if (t.nks > 1) {
-    // split K: one sub-tile per leading wave (nsub <= 4)
+    // split K over nks pieces on consecutive CUs (one sub-tile per leading
+    // wave, nsub <= 4).  Pieces 1.. publish their partial tiles into this
+    // layer's slots with the lowest bit of every word set; piece 0 polls the
+    // slots, adds the partials to its own in piece order, clears the slots
+    // (it is their only reader; the next write is a step later) and runs the
+    // epilogue.
     const bool own = nepi > 0;
     float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
     if (own) owned_values(0, val, up);
-    float* pb = A->part + (size_t)(t.part_slot + t.ks) * 1024 + w * 256;
-    if (own) {
+    float* const pl = A->part + ((size_t)t.layer * A->part_blocks + t.part_slot) * 1024 + w * 256;
+    if (own && t.ks > 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) co_storef(pb, (uint32_t)((((lane >> 4) + 4 * j) * 16 + row) * 4), val[j]);
+      for (int j = 0; j < 4; ++j)
+        co_store_tag(pl, (uint32_t)(((size_t)t.ks * 1024 + ((lane >> 4) + 4 * j) * 16 + row) * 4), val[j], 1u);
     }
-    wait_mem();
-    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
-    if (w == 0 && lane == 0) {
-      uint32_t* gc = A->grp_ctr + A->grp_off[t.stage] + t.group;
-      uint32_t old = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int fin = (int)old == t.nks - 1;
-      if (fin) __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lds_st_rel(&c->fin, fin);
-    }
-    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
-    const bool fin = lds_ld_acq(&c->fin) != 0;
-    if (own && fin) {
-      const float* p0 = A->part + (size_t)t.part_slot * 1024 + w * 256;
-      // sum the pieces in piece order, kSumBatch pieces' loads in flight at once
-      constexpr int kSumBatch = 8;
+    if (own && t.ks == 0) {
+      constexpr int kSumBatch = 4;
       const bool gu_up = t.stage == ST_GU && row < 8;
+      for (int k0 = 1; k0 < t.nks; k0 += kSumBatch) {
+        uint32_t pv[kSumBatch][4], pu[kSumBatch][4];
+        Spin sp = spin_start();
+        for (;;) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        val[j] = 0.f;
-        up[j] = 0.f;
-      }
-      for (int k0 = 0; k0 < t.nks; k0 += kSumBatch) {
-        float pv[kSumBatch][4], pu[kSumBatch][4];
+          for (int u = 0; u < kSumBatch; ++u)
 #pragma unroll
-        for (int u = 0; u < kSumBatch; ++u)
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t e = (uint32_t)((k0 + u) * 1024 + ((lane >> 4) + 4 * j) * 16 + row);
+              const bool ok = k0 + u < t.nks;
+              pv[u][j] = ok ? co_load4(pl, e * 4) : 1u;
+              pu[u][j] = ok && gu_up ? co_load4(pl, (e + 8) * 4) : 1u;
+            }
+          uint32_t flags = 1u;
+#pragma unroll
+          for (int u = 0; u < kSumBatch; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) flags &= pv[u][j] & pu[u][j];
+          if (__all((flags & 1u) != 0)) break;
+          if (!poll_ok(A, c, sp)) return false;
+        }
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u) {
+          if (k0 + u >= t.nks) break;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int e = ((lane >> 4) + 4 * j) * 16 + row;
-            const bool ok = k0 + u < t.nks;
-            pv[u][j] = ok ? co_loadf(p0, (uint32_t)(((size_t)(k0 + u) * 1024 + e) * 4)) : 0.f;
-            pu[u][j] = ok && gu_up ? co_loadf(p0, (uint32_t)(((size_t)(k0 + u) * 1024 + e + 8) * 4)) : 0.f;
+            co_store4(pl, (uint32_t)(((size_t)(k0 + u) * 1024 + ((lane >> 4) + 4 * j) * 16 + row) * 4), 0u);
+            val[j] += __uint_as_float(untag(pv[u][j]));
+            up[j] += gu_up ? __uint_as_float(untag(pu[u][j])) : 0.f;
           }
-#pragma unroll
-        for (int u = 0; u < kSumBatch; ++u)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            val[j] += pv[u][j];
-            up[j] += pu[u][j];
-          }
+        }
       }
       const int lr0 = tile_row0(0);
 #pragma unroll
