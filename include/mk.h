@@ -8,11 +8,14 @@
  * RMSNorm, LM head and greedy argmax.  This is the decode step of the
  * ForgeMegakernel paper summary ("2.1 The decode step"), kept inside one host
  * launch as its "2.3 Megakernels" section describes, with per-CU instruction
- * streams and dependency counters in place of grid-wide barriers ("4.1 The
- * universal knowledge base and the milestones"; Cohere engine digest:
+ * streams and fine-grained dependencies in place of grid-wide barriers ("4.1
+ * The universal knowledge base and the milestones"; Cohere engine digest:
  * persistent kernel with one block per SM, task descriptors, counter-based
  * barriers in global memory, weights streamed before their activation
- * dependencies are met).
+ * dependencies are met).  The dependencies are carried by the data itself:
+ * every activation word handed between compute units holds a per-sequence
+ * step tag in its lowest mantissa bit that the consumer polls for (see
+ * mk_copy_hidden and mk_reset).
  *
  * Conventions for every entry point:
  *   - returns MK_OK (0) or a negative MK_ERR_* code; nothing aborts and no
