@@ -199,7 +199,7 @@ struct CState {
   uint64_t t_epi;     // trace: ticks spent in reductions and epilogues
   int gen;      // compute-barrier generation
   int q;        // chunk sequence number of the current task's first chunk
-  int last_dep; // counter of the last dependency already satisfied
+  int last_dep; // unused: keeps the measured layout of the control block
   int x_stage, x_layer, x_k0, x_k1;  // signature of the staged input slice
   int synced;   // every compute wave passed a barrier after its last read of the staging buffer
   int r_stage, r_layer;              // stage whose RMS scales are in Ctrl::rms
@@ -209,9 +209,9 @@ struct Ctrl {
   CState cs[kComputeWaves];  // per compute wave
   int ready[kMaxSlots];
   int freed[kMaxSlots];
-  int dep;
+  int dep;  // unused (layout)
   int bar;
-  int fin;
+  int fin;  // unused (layout)
   int abort;
   unsigned long long lmkey[kMaxBatch];  // this CU's best LM-head key per sequence
   int pos[kMaxBatch];
