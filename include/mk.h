@@ -114,7 +114,10 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
  *   logits_out        device float [batch][vocab], written;
  *   next_tokens_out   device int32 [batch] greedy argmax (lowest index wins a
  *                     tie), written; may be NULL.
- * batch == 0 is a no-op.  Errors detectable on the host return an error code
+ * batch == 0 is a no-op.  Each call passes per-step values to its launch
+ * (the sequences' step tags, the counter bank), so a launch captured into a
+ * HIP graph must not be replayed as a later step.  Errors detectable on the
+ * host return an error code
  * before anything is enqueued (MK_ERR_UNSUPPORTED when n_kv_heads x batch x
  * kv->seq_cap reaches 2^31: attention counts its rows in 32 bits); data
  * errors are reported by mk_get_status. */
