@@ -54,7 +54,9 @@ class PlanStats(ctypes.Structure):
                 ("n_counters", ctypes.c_int32), ("mfma", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("max_cu_weight_bytes", ctypes.c_int64), ("stage_balance_min", ctypes.c_double),
                 ("stage_tasks", ctypes.c_int32 * 6), ("stage_ksplit", ctypes.c_int32 * 6),
-                ("stage_rows_per_task", ctypes.c_int32 * 6)]
+                ("stage_rows_per_task", ctypes.c_int32 * 6), ("stage_cus", ctypes.c_int32 * 6),
+                ("stage_shared_prev", ctypes.c_int32 * 6), ("attn_slot_cap", ctypes.c_int32),
+                ("attn_slots_valid", ctypes.c_int32)]
 
 
 EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
@@ -108,7 +110,7 @@ def plan(shape, batch: int, n_cu: int = 256, max_batch: int = 16, max_seq: int =
     cfg = model_cfg(shape, max_batch, max_seq)
     _check(lib().mk_plan(ctypes.byref(cfg), int(batch), int(n_cu), ctypes.byref(st)), "mk_plan")
     out = {k: getattr(st, k) for k, _ in PlanStats._fields_}
-    for k in ("stage_tasks", "stage_ksplit", "stage_rows_per_task"):
+    for k in ("stage_tasks", "stage_ksplit", "stage_rows_per_task", "stage_cus", "stage_shared_prev"):
         out[k] = list(out[k])
     return out
 

@@ -149,6 +149,41 @@ int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats*
     out->stage_ksplit[i] = P.stage_ksplit[i];
     out->stage_rows_per_task[i] = P.stage_rows[i];
   }
+  // placement of one layer: which CUs run each stage
+  {
+    const int L = cfg->n_layers, lay = L > 1 ? 1 : 0;
+    auto cus_of = [&](int stage, int layer) {
+      std::vector<char> u(n_cu, 0);
+      for (int c = 0; c < n_cu; ++c)
+        for (int k = P.task_off[c]; k < P.task_off[c + 1]; ++k)
+          if (P.tasks[k].stage == stage && P.tasks[k].layer == layer && P.tasks[k].type == TT_GEMV) u[c] = 1;
+      return u;
+    };
+    const int* m = P.attn_map + (size_t)lay * (n_cu + 1);
+    std::vector<char> attn(n_cu, 1);
+    if (m[n_cu] > 0)
+      for (int c = 0; c < n_cu; ++c) attn[c] = m[c] < m[n_cu];
+    std::vector<char> sets[6] = {cus_of(ST_QKV, lay), attn, cus_of(ST_O, lay), cus_of(ST_GU, lay),
+                                 cus_of(ST_DOWN, lay), cus_of(ST_LM, L)};
+    std::vector<char> prev[6] = {lay > 0 ? cus_of(ST_DOWN, lay - 1) : std::vector<char>(n_cu, 0), sets[0], sets[1],
+                                 sets[2], sets[3], cus_of(ST_DOWN, L - 1)};
+    for (int i = 0; i < 6; ++i)
+      for (int c = 0; c < n_cu; ++c) {
+        out->stage_cus[i] += sets[i][c];
+        out->stage_shared_prev[i] += sets[i][c] && prev[i][c];
+      }
+    out->attn_slot_cap = m[n_cu];
+    int valid = 1;
+    for (int l = 0; l < L && valid; ++l) {
+      std::vector<char> seen(n_cu, 0);
+      for (int c = 0; c < n_cu; ++c) {
+        const int v = P.attn_map[(size_t)l * (n_cu + 1) + c];
+        if (v < 0 || v >= n_cu || seen[v]) valid = 0;
+        else seen[v] = 1;
+      }
+    }
+    out->attn_slots_valid = valid;
+  }
   free_plan(&P);
   return MK_OK;
 }

@@ -200,6 +200,14 @@ typedef struct {
   int32_t stage_tasks[6];       /* tasks per layer-0 stage: QKV, ATTN, O, GU, DOWN, and LM */
   int32_t stage_ksplit[6];      /* K-splits chosen per stage (ATTN entry 0) */
   int32_t stage_rows_per_task[6];
+  /* placement of layer 1 (layer 0 when there is one layer), same stage order:
+   * CUs that run a task of the stage (attention: the CUs of its slot cap,
+   * all CUs without a cap), and how many of them also ran the stage before
+   * (QKV: the previous layer's down projection; LM head: the last one) */
+  int32_t stage_cus[6];
+  int32_t stage_shared_prev[6];
+  int32_t attn_slot_cap;        /* attention slot cap of that layer (0: none) */
+  int32_t attn_slots_valid;     /* 1: every layer's attention slots are a permutation of the CUs */
 } mk_plan_stats;
 
 int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats* out);
