@@ -68,6 +68,7 @@ struct mk_handle {
   uint64_t step = 0;
   uint64_t* trace = nullptr;   // MK_TRACE=<tasks per CU>: per-task timestamps + per-CU wait totals
   int trace_cap = 0;
+  int attn_pad = 0;            // attention partition: empty rows ahead of each segment (upper bound)
 };
 
 extern "C" {
@@ -329,6 +330,12 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
       return MK_ERR_HIP;
     }
   }
+  // A CU whose attention rows cross into a new segment runs a second piece
+  // (query load, wave merge, partial publish) and usually finishes that
+  // segment: padding each segment's start charges it about 256 KB of K/V
+  // rows' worth of time (512 rows at head_dim 128; the kernel caps the pad
+  // at a quarter of a CU's rows).
+  h->attn_pad = std::max(0, env_int("MK_ATTN_PAD", (256 << 10) / (4 * cfg->head_dim)));
   h->trace_cap = env_int("MK_TRACE", 0);
   if (h->trace_cap > 0) {
     size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * kStatWords) * 8;
@@ -466,6 +473,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.timeout_ticks = h->timeout_ticks;
   A.trace = h->trace;
   A.trace_cap = h->trace_cap;
+  A.attn_pad = h->attn_pad;
   if (launch_step(A, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   h->rowtag = A.rowtag;
   h->step += 1;

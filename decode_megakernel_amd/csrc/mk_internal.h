@@ -159,6 +159,7 @@ struct DevArgs {
   uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
   uint64_t* trace;          // optional per-task timestamps [ncu][trace_cap][4], NULL = off
   int32_t trace_cap;
+  int32_t attn_pad;         // attention partition: empty rows ahead of each segment (upper bound)
 };
 
 // Host planner --------------------------------------------------------------

@@ -426,9 +426,11 @@ __device__ __forceinline__ const uint16_t* row_ptr(DArgs A, int st, int l, int l
 
 // ---------------------------------------------------- attention partition
 // The flattened attention work of a step is the (sequence, kv-head, position)
-// rows in that order; CU c owns rows [W*c/ncu, W*(c+1)/ncu).  Every CU derives
-// the same partition from seq_lens, so a ragged batch is balanced without a
-// host round trip and without broadcasting one sequence's position.
+// rows in that order, each (sequence, kv-head) segment preceded by `pad`
+// empty rows; CU c owns positions [W*c/ncu, W*(c+1)/ncu) of that order.
+// Every CU derives the same partition from seq_lens, so a ragged batch is
+// balanced without a host round trip and without broadcasting one
+// sequence's position.
 struct Piece {
   int i, g, j0, j1, sid, ncached, nch, has_new;
   long long seg_start;
@@ -446,8 +448,8 @@ __device__ __forceinline__ long long attn_total_r(const SeqLens& sl, int b, int 
     if (i < b) W += sl.v[i];
   return W * nkv;
 }
-__device__ __forceinline__ bool next_piece_r(const SeqLens& sl, int b, int nkv, int rpc, long long& pos, long long hi,
-                                             Piece& P) {
+__device__ __forceinline__ bool next_piece_r(const SeqLens& sl, int b, int nkv, int rpc, int pad, long long& pos,
+                                             long long hi, Piece& P) {
   if (pos >= hi) return false;
   long long acc = 0;
   int i = 0, s = sl.v[0];
@@ -455,7 +457,7 @@ __device__ __forceinline__ bool next_piece_r(const SeqLens& sl, int b, int nkv, 
 #pragma unroll
   for (int k = 0; k < kMaxBatch; ++k) {
     if (!found && k < b) {
-      const long long seg = (long long)nkv * sl.v[k];
+      const long long seg = (long long)nkv * (sl.v[k] + pad);
       if (pos < acc + seg || k == b - 1) {
         i = k;
         s = sl.v[k];
@@ -465,18 +467,30 @@ __device__ __forceinline__ bool next_piece_r(const SeqLens& sl, int b, int nkv, 
       }
     }
   }
-  // off < nkv * s < 2^31 (the host rejects larger caches): 32-bit division
+  const int sv = s + pad;
+  // off < nkv * sv < 2^31 (the host rejects larger caches): 32-bit division
   const uint32_t off = (uint32_t)(pos - acc);
-  P.i = i;
-  P.g = (int)(off / (uint32_t)s);
-  P.j0 = (int)(off - (uint32_t)P.g * (uint32_t)s);
-  long long take = s - P.j0;
+  const int g = (int)(off / (uint32_t)sv);
+  int jv = (int)(off - (uint32_t)g * (uint32_t)sv);
+  if (jv < pad) {
+    // padding ahead of the segment's rows: skip it
+    if (hi - pos <= pad - jv) {
+      pos = hi;
+      return false;
+    }
+    pos += pad - jv;
+    jv = pad;
+  }
+  long long take = sv - jv;
   if (hi - pos < take) take = hi - pos;
+  P.i = i;
+  P.g = g;
+  P.j0 = jv - pad;
   P.j1 = P.j0 + (int)take;
-  P.sid = i * nkv + P.g;
-  P.seg_start = acc + (long long)P.g * s;
+  P.sid = i * nkv + g;
+  P.seg_start = acc + (long long)g * sv + pad;
   const int p = s - 1;
-  int nc = (P.j1 < p ? P.j1 : p) - P.j0;
+  const int nc = (P.j1 < p ? P.j1 : p) - P.j0;
   P.ncached = nc > 0 ? nc : 0;
   P.has_new = P.j1 == s;
   P.nch = (P.ncached + rpc - 1) / rpc;
@@ -523,28 +537,55 @@ __device__ __forceinline__ int attn_nacu(DArgs A, int l, long long W) {
   return n;
 }
 
-__device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rpc, long long& pos, long long hi, Piece& P) {
+// Empty rows ahead of every segment in the flattened order: a CU whose range
+// crosses a segment start gets that many fewer rows for its second piece.
+// At most a quarter of a CU's share, and none when the padded order would
+// leave 32-bit range.
+__device__ __forceinline__ int attn_pad_rows(DArgs A, long long W, int nacu) {
+  long long pad = W / (4LL * nacu);
+  if (pad > A->attn_pad) pad = A->attn_pad;
+  if (W + (long long)A->b * A->nkv * pad >= (1LL << 31)) pad = 0;
+  return (int)pad;
+}
+// flattened length of the step's attention work with `pad` empty rows per segment
+__device__ __forceinline__ long long attn_padded(DArgs A, long long W, int pad) {
+  return W + (long long)A->b * A->nkv * pad;
+}
+
+__device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rpc, int pad, long long& pos, long long hi,
+                                           Piece& P) {
   if (pos >= hi) return false;
   long long acc = 0;
   int i = 0;
   for (; i < b - 1; ++i) {
-    long long seg = (long long)nkv * c->slen[i];
+    const long long seg = (long long)nkv * (c->slen[i] + pad);
     if (pos < acc + seg) break;
     acc += seg;
   }
-  const int s = c->slen[i];
-  // off < nkv * s < 2^31 (the host rejects larger caches): 32-bit division
+  const int s = c->slen[i], sv = s + pad;
+  // off < nkv * sv < 2^31 (the host rejects larger caches): 32-bit division
   const uint32_t off = (uint32_t)(pos - acc);
-  P.i = i;
-  P.g = (int)(off / (uint32_t)s);
-  P.j0 = (int)(off - (uint32_t)P.g * (uint32_t)s);
-  long long take = s - P.j0;
+  const int g = (int)(off / (uint32_t)sv);
+  int jv = (int)(off - (uint32_t)g * (uint32_t)sv);
+  if (jv < pad) {
+    // padding ahead of the segment's rows: skip it
+    if (hi - pos <= pad - jv) {
+      pos = hi;
+      return false;
+    }
+    pos += pad - jv;
+    jv = pad;
+  }
+  long long take = sv - jv;
   if (hi - pos < take) take = hi - pos;
+  P.i = i;
+  P.g = g;
+  P.j0 = jv - pad;
   P.j1 = P.j0 + (int)take;
-  P.sid = i * nkv + P.g;
-  P.seg_start = acc + (long long)P.g * s;
+  P.sid = i * nkv + g;
+  P.seg_start = acc + (long long)g * sv + pad;
   const int p = s - 1;
-  int nc = (P.j1 < p ? P.j1 : p) - P.j0;
+  const int nc = (P.j1 < p ? P.j1 : p) - P.j0;
   P.ncached = nc > 0 ? nc : 0;
   P.has_new = P.j1 == s;
   P.nch = (P.ncached + rpc - 1) / rpc;
@@ -759,13 +800,15 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
       }
       qbase += nch;
     } else if (t.type == TT_ATTN) {
-      const long long W = attn_total_r(sl, A->b, A->nkv);
-      const int nacu = attn_nacu(A, t.layer, W), slot = attn_slot(A, t.layer, cu);
+      const long long W0 = attn_total_r(sl, A->b, A->nkv);
+      const int nacu = attn_nacu(A, t.layer, W0), slot = attn_slot(A, t.layer, cu);
+      const int pad = attn_pad_rows(A, W0, nacu);
+      const long long W = attn_padded(A, W0, pad);
       long long pos = slot < nacu ? cu_lo(slot, W, nacu) : W;
       const long long hi = slot < nacu ? cu_lo(slot + 1, W, nacu) : W;
       Piece P;
       int pbase = qbase;
-      while (next_piece_r(sl, A->b, A->nkv, rpc, pos, hi, P)) {
+      while (next_piece_r(sl, A->b, A->nkv, rpc, pad, pos, hi, P)) {
         const size_t head = (((size_t)t.layer * A->kv_bcap + P.i) * A->nkv + P.g) * A->kv_scap;
         for (int ch = R.q - pbase; ch < P.nch; ch += kLoaderWaves) {
           if (!ring_acquire(A, c, R, lane)) return;
@@ -796,12 +839,14 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
 __device__ __forceinline__ int attn_task_chunks(DArgs A, int cu, int l, int rpc) {
   A = uni(A);
   const Ctrl* c = ctrl_block(A);
-  long long W = attn_total(c, A->b, A->nkv);
-  const int nacu = attn_nacu(A, l, W), slot = attn_slot(A, l, cu);
+  const long long W0 = attn_total(c, A->b, A->nkv);
+  const int nacu = attn_nacu(A, l, W0), slot = attn_slot(A, l, cu);
+  const int pad = attn_pad_rows(A, W0, nacu);
+  const long long W = attn_padded(A, W0, pad);
   long long pos = slot < nacu ? cu_lo(slot, W, nacu) : W, hi = slot < nacu ? cu_lo(slot + 1, W, nacu) : W;
   Piece P;
   int n = 0;
-  while (next_piece(c, A->b, A->nkv, rpc, pos, hi, P)) n += P.nch;
+  while (next_piece(c, A->b, A->nkv, rpc, pad, pos, hi, P)) n += P.nch;
   return n;
 }
 
@@ -1720,9 +1765,11 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   const int l = t.layer, G = A->G, e0 = (lane % LPR) * 8, gi = lane / LPR;
   const int r16 = lane & 15, lr = lane >> 4;  // MFMA output layout: row r16 of a block, heads 4 lr + i
   const float qscale = kLog2e / sqrtf((float)HD);
-  const long long W = attn_total(c, A->b, A->nkv);
+  const long long W0 = attn_total(c, A->b, A->nkv);
   // this CU's slot: pieces, partial slots and the finisher role go by slot
-  const int nacu = attn_nacu(A, t.layer, W), slot = attn_slot(A, t.layer, cu);
+  const int nacu = attn_nacu(A, t.layer, W0), slot = attn_slot(A, t.layer, cu);
+  const int pad = attn_pad_rows(A, W0, nacu);
+  const long long W = attn_padded(A, W0, pad);  // flattened (padded) length: all positions below are in it
   long long pos = slot < nacu ? cu_lo(slot, W, nacu) : W, hi = slot < nacu ? cu_lo(slot + 1, W, nacu) : W;
   Piece P;
   int qc = s.q, pidx = 0;
@@ -1894,7 +1941,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
 #pragma unroll
       for (int k = 0; k < kAttnBatch; ++k) {
         bi[k] = bg[k] = bnew[k] = 0;
-        if (next_piece(c, A->b, A->nkv, RPC, tpos, hi, Q)) {
+        if (next_piece(c, A->b, A->nkv, RPC, pad, tpos, hi, Q)) {
           bi[k] = Q.i;
           bg[k] = Q.g;
           bnew[k] = Q.has_new;
@@ -1902,6 +1949,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         }
       }
     }
+    // the rest of the range is segment padding: no piece left (uniform
+    // over the compute waves, before any barrier of the batch)
+    if (nbp == 0) break;
     const int nrows = nbp * (GM + 1);  // rows (piece, h): h < GM queries, h == GM the new K / V
     qmark(0);
     for (int r0 = 0; r0 < nrows; r0 += kComputeWaves * RP) {
@@ -1979,7 +2029,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     qmark(3);
     amark(0);
     for (int bk = 0; bk < nbp; ++bk) {
-    next_piece(c, A->b, A->nkv, RPC, bpos, hi, P);
+    next_piece(c, A->b, A->nkv, RPC, pad, bpos, hi, P);
     if (ast) trace_add(ast + 7, 1);
     const float* qk = qs + (size_t)bk * GM * HD;  // this piece's scaled queries
     u32x4 qa_hi[NDS], qa_lo[NDS];
