@@ -542,8 +542,9 @@ __device__ __forceinline__ int attn_nacu(DArgs A, int l, long long W) {
 // At most a quarter of a CU's share, and none when the padded order would
 // leave 32-bit range.
 __device__ __forceinline__ int attn_pad_rows(DArgs A, long long W, int nacu) {
-  long long pad = W / (4LL * nacu);
-  if (pad > A->attn_pad) pad = A->attn_pad;
+  // W < 2^31 (the host rejects larger caches): 32-bit division
+  uint32_t pad = (uint32_t)W / (uint32_t)(4 * nacu);
+  if (pad > (uint32_t)A->attn_pad) pad = (uint32_t)A->attn_pad;
   if (W + (long long)A->b * A->nkv * pad >= (1LL << 31)) pad = 0;
   return (int)pad;
 }
