@@ -4,17 +4,19 @@
 // see mk_plan.cpp).  Inside a work-group:
 //   * 3 loader waves stream every input-independent byte the CU's tasks need
 //     (weight tiles, cached K/V rows) from HBM into an LDS ring with
-//     non-temporal loads.  They never wait on a dependency counter, so weights
-//     for later tasks arrive while the CU is still waiting for activations
-//     (the weight prefetch of the Cohere megakernel digest; the shared-memory
+//     non-temporal loads.  They never wait on a dependency, so weights for
+//     later tasks arrive while the CU is still waiting for activations (the
+//     weight prefetch of the Cohere megakernel digest; the shared-memory
 //     buffer pool of the ForgeMegakernel milestones).
-//   * 4 compute waves wait on dependency counters, stage the activation slice
-//     into LDS, run the GEMV (VALU dot2 for small batches, MFMA 16x16x32 bf16
-//     for batch >= 8) or split-KV attention tiles out of the ring, and write
-//     their outputs with fused epilogues (residual add, next RMSNorm's sum of
-//     squares, SiLU-gate, RoPE, KV store, argmax).
-// Cross-CU exchange uses device-coherent (sc1) loads and stores plus 64-way
-// sharded counters; no agent-scope cache fences are issued on the hot path.
+//   * 4 compute waves poll their step-tagged inputs until every word carries
+//     this step's tag, stage the activation slice into LDS, run the GEMV
+//     (VALU dot2 for small batches, MFMA 16x16x32 bf16 for batch >= 8) or
+//     split-KV attention tiles out of the ring, and write their outputs with
+//     fused epilogues (residual add, next RMSNorm's sum of squares, SiLU-gate,
+//     RoPE, KV store, argmax).
+// Cross-CU exchange uses device-coherent (sc1) loads and stores; 64-way
+// sharded counters remain only for the LM head's completion (greedy tokens).
+// No agent-scope cache fences are issued on the hot path.
 #include <hip/hip_runtime.h>
 
 #include "mk_internal.h"

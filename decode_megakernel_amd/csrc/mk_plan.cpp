@@ -1,10 +1,13 @@
 // Host-side task-graph builder: tiles one decode step into per-CU instruction
 // streams and proves the schedule covers every weight exactly once and cannot
-// deadlock.  The per-CU streams with dependency counters in place of
+// deadlock.  The per-CU streams with fine-grained dependencies in place of
 // grid-wide barriers follow the ForgeMegakernel milestones ("4.1 The universal
 // knowledge base and the milestones": per-SM instruction streams, dependency
 // counters, buffer pool); the one-block-per-SM task-descriptor execution model
-// follows the Cohere megakernel digest.
+// follows the Cohere megakernel digest.  Each task's dependency is recorded as
+// a counter and the deadlock check runs over those counts; on the device the
+// hand-offs poll step-tagged data instead, and only the LM head's completion
+// is still counted.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
