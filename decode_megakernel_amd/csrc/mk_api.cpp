@@ -26,6 +26,8 @@ namespace {
 
 struct GraphDev {
   Plan plan;
+  int nslot = 0;  // LDS ring slots of this batch size's launches
+  int xb = 0;     // LDS bytes left to stage GEMV inputs
   Task* d_tasks = nullptr;
   int* d_off = nullptr;
   int* d_expect = nullptr;
@@ -47,8 +49,9 @@ struct mk_handle {
   mk_model_cfg cfg;
   int device = 0;
   int ncu = 0;
-  int nslot = 6;
+  int nslot = 7;    // ring slots with no batch rule applied (the smallest staging buffer)
   int xb = 0;
+  int lds_max = 0;  // LDS bytes per work-group
   int mfma_min_batch = 8;
   uint64_t timeout_ticks = 0;
   LayerW* d_layers = nullptr;
@@ -128,12 +131,30 @@ static int xb_for(int lds_max, int nslot) {
   return (int)xb;
 }
 
+// Ring slots for a batch: 7 by default.  An MFMA batch (>= mfma_min) whose
+// GEMV input windows (K blocks staged at once, 4 bytes per element and
+// sequence) grow when one slot's 16 KB goes to the staging buffer takes 6:
+// fewer restaging round trips outweigh the shallower prefetch (Llama-3-8B
+// b9 7.29 -> 7.12 ms; at batch 16 the window stays one block and 6 slots are
+// slower).  MK_NSLOT, when set, fixes the count for every batch.
+static int nslot_for(int lds_max, int b, int mfma_min) {
+  const char* v = getenv("MK_NSLOT");
+  int n = (v && *v) ? atoi(v) : 7;
+  if (!(v && *v) && b >= mfma_min) {
+    auto wkb = [&](int nslot) { return std::max(1, ((xb_for(lds_max, nslot) / (4 * b)) - 8) / kKBlock); };
+    if (wkb(6) > wkb(7)) n = 6;
+  }
+  // a loader wave publishes a chunk only after issuing its next one, so the
+  // ring must hold more chunks than there are loader waves
+  return std::min(kMaxSlots, std::max(kLoaderWaves + 1, n));
+}
+
 int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats* out) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!out || n_cu < 1 || batch < 1 || batch > cfg->max_batch) return MK_ERR_INVALID_ARG;
-  const int nslot = env_int("MK_NSLOT", 7);
-  PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot), std::min(8, std::max(1, env_int("MK_MFMA_MIN_BATCH", 8))));
+  const int mfma_min = std::min(8, std::max(1, env_int("MK_MFMA_MIN_BATCH", 8)));
+  PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot_for(163840, batch, mfma_min)), mfma_min);
   Plan P;
   rc = build_plan(pc, batch, &P);
   if (rc) return rc;
@@ -218,12 +239,10 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   }
   h->ncu = env_int("MK_NUM_CU", prop.multiProcessorCount);
   if (h->ncu < 1 || h->ncu > prop.multiProcessorCount) h->ncu = prop.multiProcessorCount;
-  h->nslot = env_int("MK_NSLOT", 7);
-  // a loader wave publishes a chunk only after issuing its next one, so the
-  // ring must hold more chunks than there are loader waves
-  if (h->nslot < kLoaderWaves + 1) h->nslot = kLoaderWaves + 1;
-  if (h->nslot > kMaxSlots) h->nslot = kMaxSlots;
-  h->xb = xb_for((int)prop.sharedMemPerBlock, h->nslot);
+  h->lds_max = (int)prop.sharedMemPerBlock;
+  // the smallest staging buffer any batch gets (the most ring slots)
+  h->nslot = std::max(nslot_for(h->lds_max, 1, 1 << 30), nslot_for(h->lds_max, cfg->max_batch, 1 << 30));
+  h->xb = xb_for(h->lds_max, h->nslot);
   // the staging buffer holds attention's softmax states, and one 512-wide K
   // block of every sequence's input as bf16 hi + lo halves (plus padding)
   if (h->xb < kAttnStateBytes || h->xb < cfg->max_batch * (kKBlock + 8) * 4) {
@@ -369,7 +388,9 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
     return MK_OK;
   }
   GraphDev g;
-  PlanCfg pc = plan_cfg(&h->cfg, h->ncu, h->xb, h->mfma_min_batch);
+  g.nslot = nslot_for(h->lds_max, b, h->mfma_min_batch);
+  g.xb = xb_for(h->lds_max, g.nslot);
+  PlanCfg pc = plan_cfg(&h->cfg, h->ncu, g.xb, h->mfma_min_batch);
   int rc = build_plan(pc, b, &g.plan);
   if (rc) return rc;
   const Plan& P = g.plan;
@@ -467,8 +488,8 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.bank_words = h->bank_words;
   A.part_blocks = std::max(1, g->plan.part_blocks);
   A.ncu = h->ncu;
-  A.nslot = h->nslot;
-  A.xb_bytes = h->xb;
+  A.nslot = g->nslot;
+  A.xb_bytes = g->xb;
   A.mfma = g->plan.mfma;
   A.timeout_ticks = h->timeout_ticks;
   A.trace = h->trace;
