@@ -353,7 +353,7 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   // (query load, wave merge, partial publish) and usually finishes that
   // segment: padding each segment's start charges it about 256 KB of K/V
   // rows' worth of time (512 rows at head_dim 128; the kernel caps the pad
-  // at a quarter of a CU's rows).
+  // at half a CU's rows).
   h->attn_pad = std::max(0, env_int("MK_ATTN_PAD", (256 << 10) / (4 * cfg->head_dim)));
   h->trace_cap = env_int("MK_TRACE", 0);
   if (h->trace_cap > 0) {

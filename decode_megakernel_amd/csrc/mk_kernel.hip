@@ -541,11 +541,11 @@ __device__ __forceinline__ int attn_nacu(DArgs A, int l, long long W) {
 
 // Empty rows ahead of every segment in the flattened order: a CU whose range
 // crosses a segment start gets that many fewer rows for its second piece.
-// At most a quarter of a CU's share, and none when the padded order would
-// leave 32-bit range.
+// At most half a CU's share (so no CU's range lies inside padding), and none
+// when the padded order would leave 32-bit range.
 __device__ __forceinline__ int attn_pad_rows(DArgs A, long long W, int nacu) {
   // W < 2^31 (the host rejects larger caches): 32-bit division
-  uint32_t pad = (uint32_t)W / (uint32_t)(4 * nacu);
+  uint32_t pad = (uint32_t)W / (uint32_t)(2 * nacu);
   if (pad > (uint32_t)A->attn_pad) pad = (uint32_t)A->attn_pad;
   if (W + (long long)A->b * A->nkv * pad >= (1LL << 31)) pad = 0;
   return (int)pad;
