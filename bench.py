@@ -22,7 +22,9 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DEFAULT_WORKLOAD = "qwen3-0.6b-b1"
+DEFAULT_WORKLOAD = "llama2-13b-b16"
+# workloads measured beside the headline: (workload, phases timed)
+PER_CONFIG = ["llama3.2-1b-b8", "llama3-8b-b1", "llama3-8b-b8to9"]
 
 
 def kernel_sha() -> str:
@@ -36,11 +38,13 @@ def kernel_sha() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--phase", type=int, default=-1, help="phase index (default: the last phase)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the headline workload")
+    ap.add_argument("--per-config-steps", type=int, default=10)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling profiler byte counters) and exit")
     return ap.parse_args()
@@ -57,35 +61,114 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "launches": 3}))
 
 
-def setup(wl, phase_idx, steps_total):
-    """Weights, KV cache and per-step input buffers on the GPU."""
-    import torch
-    from mkinputs import make_weights, make_kv_cache, draw_contexts, draw_tokens, kv_capacity
-    shape = wl.shape
-    phase = wl.phases[phase_idx]
-    b = phase.batch
-    ctx = draw_contexts(wl.seed, wl.batch_cap, wl.ctx_lo, wl.ctx_hi)
-    # earlier phases advance their sequences before this phase starts
-    start = [0] * wl.batch_cap
-    for p in wl.phases[:phase_idx]:
-        for i in range(p.batch):
-            start[i] += p.steps
-    ctx_now = [ctx[i] + start[i] for i in range(b)]
-    seq_cap = kv_capacity(max(ctx_now) + 1, steps_total)
-    weights = make_weights(shape, wl.seed, device="cuda")
-    K, V = make_kv_cache(shape, wl.seed, ctx_now, wl.batch_cap, seq_cap, device="cuda")
-    toks = draw_tokens(wl.seed, b, shape.vocab)
-    pos = torch.tensor([[c + s for c in ctx_now] for s in range(steps_total)], dtype=torch.int32, device="cuda")
-    lens = pos + 1
-    tok = torch.zeros((2, b), dtype=torch.int32, device="cuda")
-    tok[0] = torch.tensor(toks, dtype=torch.int32, device="cuda")
-    logits = torch.empty((b, shape.vocab), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    return dict(shape=shape, b=b, ctx=ctx_now, seq_cap=seq_cap, weights=weights, K=K, V=V, pos=pos, lens=lens,
-                tok=tok, logits=logits)
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
-def cpu_baseline(wl, S, host_sample_layers=None):
+class Run:
+    """A workload's weights, KV cache (every sequence's prompt in place from
+    the start) and engine on the GPU; phases run back to back on the same
+    engine and cache, so a sequence that joins finds the others mid-run."""
+
+    def __init__(self, wl, steps_per_phase):
+        import torch
+        from mkinputs import make_weights, make_kv_cache, draw_contexts, draw_tokens, kv_capacity
+        from decode_megakernel_amd.binding import DecodeEngine
+        self.wl, self.shape = wl, wl.shape
+        self.ctx = draw_contexts(wl.seed, wl.batch_cap, wl.ctx_lo, wl.ctx_hi)
+        total = steps_per_phase * len(wl.phases)
+        self.seq_cap = kv_capacity(max(self.ctx) + 1, total)
+        self.weights = make_weights(self.shape, wl.seed, device="cuda")
+        self.K, self.V = make_kv_cache(self.shape, wl.seed, self.ctx, wl.batch_cap, self.seq_cap, device="cuda")
+        self.first_tok = torch.tensor(draw_tokens(wl.seed, wl.batch_cap, self.shape.vocab), dtype=torch.int32,
+                                      device="cuda")
+        self.tok = torch.zeros((2, wl.batch_cap), dtype=torch.int32, device="cuda")
+        self.tok[0] = self.first_tok
+        self.logits = torch.empty((wl.batch_cap, self.shape.vocab), dtype=torch.float32, device="cuda")
+        self.done = [0] * wl.batch_cap
+        self.s = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.eng = DecodeEngine(self.shape, self.weights, max_batch=wl.batch_cap, max_seq=self.seq_cap)
+        self.create_ms = (time.perf_counter() - t0) * 1e3
+
+    def phase(self, b, warmup, steps):
+        """warmup + steps chained decode steps at batch b; per-step kernel time
+        from HIP events on the launch stream, wall time of the timed steps."""
+        import torch
+        from decode_megakernel_amd.bytes_model import step_bytes
+        stream = torch.cuda.current_stream()
+        # sequences taking their first step feed their own first token
+        for i in range(b):
+            if self.done[i] == 0:
+                self.tok[self.s % 2, i] = self.first_tok[i]
+        n = warmup + steps
+        pos = torch.tensor([[self.ctx[i] + self.done[i] + k for i in range(b)] for k in range(n)], dtype=torch.int32,
+                           device="cuda")
+        lens = pos + 1
+        s0 = self.s
+
+        def step(k):
+            s = s0 + k
+            self.eng.step(self.tok[s % 2, :b], pos[k], lens[k], self.K, self.V, self.logits[:b],
+                          self.tok[(s + 1) % 2, :b], stream=stream, batch=b)
+
+        for k in range(warmup):
+            step(k)
+        torch.cuda.synchronize()
+        st = self.eng.status()
+        if st:
+            raise RuntimeError(f"device status {st:#x} during warmup")
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            starts[k].record(stream)
+            step(warmup + k)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = self.eng.status()
+        if st:
+            raise RuntimeError(f"device status {st:#x} during the timed steps")
+        per = [starts[k].elapsed_time(ends[k]) * 1e-3 for k in range(steps)]
+        nbytes = [step_bytes(self.shape, [self.ctx[i] + self.done[i] + warmup + k + 1 for i in range(b)])
+                  for k in range(steps)]
+        ctx_first = [self.ctx[i] + self.done[i] + warmup for i in range(b)]
+        for i in range(b):
+            self.done[i] += n
+        self.s += n
+        return {"batch": b, "per_step_s": per, "bytes": nbytes, "wall_s": wall, "steps": steps,
+                "context_at_first_timed_step": ctx_first}
+
+    def close(self):
+        import torch
+        self.eng.close()
+        del self.weights, self.K, self.V
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def summarize(ph):
+    from decode_megakernel_amd.bytes_model import HBM_PEAK_BYTES_PER_S
+    ks = sum(ph["per_step_s"])
+    achieved = sum(ph["bytes"]) / ks
+    srt = sorted(ph["per_step_s"])
+    return {"batch": ph["batch"], "kernel_ms_mean": round(ks / ph["steps"] * 1e3, 4),
+            "kernel_ms_median": round(srt[len(srt) // 2] * 1e3, 4),
+            "tokens_per_s": round(ph["batch"] * ph["steps"] / ph["wall_s"], 2),
+            "algorithmic_bytes_per_step": int(sum(ph["bytes"]) / ph["steps"]),
+            "achieved_GBps": round(achieved / 1e9, 1), "mbu": round(achieved / HBM_PEAK_BYTES_PER_S, 4)}
+
+
+def cpu_baseline(run, b, ctx, host_sample_layers=None):
     """The float64 oracle, as it stands, timed on the host for a bounded sample
     of the same workload: one full decode step for models up to ~1B
     parameters, otherwise a few layers plus the LM head scaled to all layers."""
@@ -97,21 +180,22 @@ def cpu_baseline(wl, S, host_sample_layers=None):
         cores = max([p.get("num_threads", 0) for p in threadpool_info()] or [os.cpu_count()])
     except Exception:
         cores = os.cpu_count()
-    shape = S["shape"]
-    b = S["b"]
+    shape = run.shape
     L = shape.n_layers
     n_params_layer = (shape.hidden * (shape.q_dim + 2 * shape.kv_dim) + shape.q_dim * shape.hidden +
                       3 * shape.hidden * shape.intermediate)
     nl = L if n_params_layer * L <= 1.2e9 else (host_sample_layers or 2)
-    names = [n for n in S["weights"] if ".layers." not in n or int(n.split(".")[2]) < nl]
-    bits = {n: bf16_bits(S["weights"][n]) for n in names}
-    kbits = bf16_bits(S["K"][:nl])
-    vbits = bf16_bits(S["V"][:nl])
+    names = [n for n in run.weights if ".layers." not in n or int(n.split(".")[2]) < nl]
+    bits = {n: bf16_bits(run.weights[n]) for n in names}
+    # the sample's prompt rows: every position below each sequence's context
+    cmax = max(ctx)
+    kbits = bf16_bits(run.K[:nl, :b, :, :cmax])
+    vbits = bf16_bits(run.V[:nl, :b, :, :cmax])
     sub = shape.replace(n_layers=nl)
     W = oracle.Weights(sub, bits, keep=False)
-    kv = oracle.KVState(sub, kbits, vbits, S["ctx"])
-    toks = [int(t) for t in S["tok"][0].cpu()]
-    pos = S["ctx"]
+    kv = oracle.KVState(sub, kbits, vbits, ctx)
+    toks = [int(t) for t in run.first_tok[:b].cpu()]
+    pos = ctx
     # repeat the sampled step until about 10 s of CPU work (at most 30 s)
     t_layers = t_head = 0.0
     reps = 0
@@ -133,6 +217,8 @@ def cpu_baseline(wl, S, host_sample_layers=None):
               f"{reps} repetitions of {nl} of {L} layers plus the LM head of one float64 oracle decode step "
               f"(batch {b}), layer time scaled to {L} layers")
     return {"value": b / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "sample": sample,
+            "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "cores_note": "cores = threads of the BLAS pool the float64 oracle ran on",
             "seconds_measured": round(t_layers + t_head, 3), "repetitions": reps}
 
 
@@ -160,78 +246,68 @@ def main():
         copy_probe()
         return
     from mkinputs import WORKLOADS
-    from decode_megakernel_amd.binding import DecodeEngine
-    from decode_megakernel_amd.bytes_model import step_bytes, HBM_PEAK_BYTES_PER_S
+    from decode_megakernel_amd.bytes_model import HBM_PEAK_BYTES_PER_S
     wl = WORKLOADS[args.workload]
-    phase_idx = args.phase if args.phase >= 0 else len(wl.phases) - 1
-    total = args.warmup + args.steps
-    S = setup(wl, phase_idx, total)
-    shape, b = S["shape"], S["b"]
-    eng = DecodeEngine(shape, S["weights"], max_batch=wl.batch_cap, max_seq=S["seq_cap"])
-    stream = torch.cuda.current_stream()
-
-    def step(s):
-        eng.step(S["tok"][s % 2], S["pos"][s], S["lens"][s], S["K"], S["V"], S["logits"], S["tok"][(s + 1) % 2],
-                 stream=stream)
-
-    t_first = time.perf_counter()
-    step(0)
-    torch.cuda.synchronize()
-    first_ms = (time.perf_counter() - t_first) * 1e3
-    for s in range(1, args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    status = eng.status()
-    if status:
-        raise RuntimeError(f"device status {status:#x} during warmup")
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record(stream)
-        step(args.warmup + k)
-        ends[k].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    status = eng.status()
-    if status:
-        raise RuntimeError(f"device status {status:#x} during the timed steps")
-    per = [starts[k].elapsed_time(ends[k]) * 1e-3 for k in range(args.steps)]
-    kernel_s = sum(per)
-    total_bytes = sum(step_bytes(shape, [c + args.warmup + k + 1 for c in S["ctx"]]) for k in range(args.steps))
-    achieved = total_bytes / kernel_s
-    tokens_per_s = b * args.steps / wall
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, S)
-    per_sorted = sorted(per)
+    n = args.warmup + args.steps
+    # the headline: the workload's last phase after its earlier ones (a batch
+    # that grows runs its first phase untimed, warmup only)
+    run = Run(wl, n)
+    for p in wl.phases[:-1]:
+        run.phase(p.batch, args.warmup, 1)
+    ph = run.phase(wl.phases[-1].batch, args.warmup, args.steps)
+    b = ph["batch"]
+    head = summarize(ph)
+    kernel_s = sum(ph["per_step_s"])
+    achieved = sum(ph["bytes"]) / kernel_s
+    cpu = None if args.no_cpu_baseline else cpu_baseline(run, b, [run.ctx[i] for i in range(b)])
+    create_ms = run.create_ms
+    run.close()
+    del run
+    per_config = {}
+    if not args.no_per_config:
+        k = args.per_config_steps
+        for key in PER_CONFIG:
+            if key == wl.key:
+                continue
+            w2 = WORKLOADS[key]
+            r2 = Run(w2, args.warmup + k)
+            rec = {"note": w2.note, "phases": []}
+            for p in w2.phases:
+                rec["phases"].append(summarize(r2.phase(p.batch, args.warmup, k)))
+            if len(rec["phases"]) == 2:
+                rec["mbu_ratio_last_to_first"] = round(rec["phases"][1]["mbu"] / rec["phases"][0]["mbu"], 4)
+            r2.close()
+            del r2
+            per_config[key] = rec
+            print(f"# per-config {key}: " + json.dumps(rec["phases"]), file=sys.stderr, flush=True)
     line = {
         "metric": "decode tokens/sec and MBU (% of 8 TB/s HBM peak) per decode step, 1 MI355X",
-        "value": round(tokens_per_s, 2),
+        "value": round(b * args.steps / ph["wall_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(ph["wall_s"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded random-init bf16 weights N(0,0.02), N(0,1) prompt KV, uniform first tokens",
-        "config": {"workload": wl.key, "shape": shape.name, "batch": b, "context_at_first_timed_step": S["ctx"],
-                   "note": wl.note},
+        "config": {"workload": wl.key, "shape": wl.shape.name, "batch": b,
+                   "context_at_first_timed_step": ph["context_at_first_timed_step"], "note": wl.note},
         "mbu": round(achieved / HBM_PEAK_BYTES_PER_S, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK_BYTES_PER_S / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_BYTES_PER_S, 4),
                      "traffic": traffic_from_profile(wl.key),
-                     "algorithmic_bytes_per_step": int(total_bytes / args.steps),
-                     "kernel_ms_mean": round(kernel_s / args.steps * 1e3, 4),
-                     "kernel_ms_median": round(per_sorted[len(per) // 2] * 1e3, 4),
-                     "kernel_ms_min": round(per_sorted[0] * 1e3, 4)},
+                     "kernel": "mk_step_kernel",
+                     "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"],
+                     "kernel_ms_mean": head["kernel_ms_mean"], "kernel_ms_median": head["kernel_ms_median"],
+                     "kernel_ms_min": round(min(ph["per_step_s"]) * 1e3, 4)},
         "cpu_baseline": cpu,
-        "first_step_ms_including_schedule_build": round(first_ms, 2),
+        "per_config": per_config,
+        "create_ms_including_all_schedules": round(create_ms, 1),
         "kernel_sha": kernel_sha(),
     }
-    eng.close()
     print(json.dumps(line), flush=True)
 
 

@@ -60,7 +60,7 @@ class PlanStats(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
-           "mk_reset", "mk_destroy", "mk_error_string", "mk_plan"]
+           "mk_reset", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
 STAT_WORDS = 80  # per-CU trace totals, see mk_copy_trace
 
@@ -82,6 +82,7 @@ def lib():
     L.mk_copy_trace.argtypes = [vp, vp, ctypes.c_int64, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
     L.mk_get_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.mk_reset.argtypes = [vp, vp]
+    L.mk_set_midstate_dump.argtypes = [vp, vp]
     L.mk_destroy.argtypes = [vp]
     L.mk_error_string.argtypes = [ctypes.c_int]
     L.mk_error_string.restype = ctypes.c_char_p
@@ -113,6 +114,11 @@ def plan(shape, batch: int, n_cu: int = 256, max_batch: int = 16, max_seq: int =
     for k in ("stage_tasks", "stage_ksplit", "stage_rows_per_task", "stage_cus", "stage_shared_prev"):
         out[k] = list(out[k])
     return out
+
+
+def torch_float32():
+    import torch
+    return torch.float32
 
 
 def _stream_handle(stream):
@@ -215,6 +221,17 @@ class DecodeEngine:
         s = ctypes.c_uint32()
         _check(lib().mk_get_status(self.handle, _stream_handle(stream), ctypes.byref(s)), "mk_get_status")
         return int(s.value)
+
+    def set_midstate_dump(self, out):
+        """Every later step also writes its residual stream into `out` (a CUDA
+        float32 tensor [n_layers+1, max_batch, hidden] the caller keeps alive);
+        None switches it off."""
+        if out is not None:
+            assert out.is_cuda and out.dtype == torch_float32() and out.is_contiguous()
+            assert tuple(out.shape) == (self.shape.n_layers + 1, self.max_batch, self.shape.hidden)
+        _check(lib().mk_set_midstate_dump(self.handle, None if out is None else out.data_ptr()),
+               "mk_set_midstate_dump")
+        self._dump = out
 
     def reset(self, stream=None):
         _check(lib().mk_reset(self.handle, _stream_handle(stream)), "mk_reset")

@@ -14,7 +14,8 @@
 #include "mk_internal.h"
 
 namespace mk {
-hipError_t launch_step(const DevArgs& A, hipStream_t stream);
+hipError_t launch_step(const DevArgs& A, hipStream_t stream, bool coop);
+hipError_t step_occupancy(size_t lds, int* blocks_per_cu);
 hipError_t launch_untag_copy(void* dst, size_t dpitch, const void* src, size_t spitch, size_t row_bytes, size_t rows,
                              hipStream_t stream);
 size_t lds_bytes(int nslot, int xb_bytes);
@@ -32,7 +33,6 @@ struct GraphDev {
   int* d_off = nullptr;
   int* d_expect = nullptr;
   int* d_attn_map = nullptr;
-  float* d_part = nullptr;
 };
 
 int env_int(const char* name, int def) {
@@ -67,7 +67,11 @@ struct mk_handle {
   float *xattn, *xmlp, *attn_out, *act;
   uint32_t *banks, *status;
   int ctr_stride = 0, bank_words = 0;
-  std::map<int, GraphDev> graphs;
+  std::map<int, GraphDev> graphs;  // one schedule per batch size 1..max_batch, built by mk_create
+  float* d_part = nullptr;          // split-K partial slots, shared by every schedule (all zero between steps)
+  size_t part_bytes = 0;
+  int coop = 1;                     // cooperative launches (co-residency guaranteed by the runtime)
+  float* dump = nullptr;            // caller's mid-state dump buffer (mk_set_midstate_dump), NULL = off
   uint64_t step = 0;
   uint64_t* trace = nullptr;   // MK_TRACE=<tasks per CU>: per-task timestamps + per-CU wait totals
   int trace_cap = 0;
@@ -87,6 +91,9 @@ const char* mk_error_string(int code) {
   }
   return "unknown error";
 }
+
+static int build_graph(mk_handle* h, int b);
+static size_t part_bytes_of(const mk_handle* h, const GraphDev& g);
 
 static int check_cfg(const mk_model_cfg* c) {
   if (!c) return MK_ERR_INVALID_ARG;
@@ -368,6 +375,39 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   h->embed = (const uint16_t*)w->embed;
   h->lm_head = cfg->tied_embeddings ? (const uint16_t*)w->embed : (const uint16_t*)w->lm_head;
   h->final_norm = (const uint16_t*)w->final_norm;
+  // every schedule the handle can run (batch 1..max_batch) is built, validated
+  // and uploaded here, so a step never allocates, copies or synchronises on
+  // the host (a new batch size mid-run is a lookup)
+  for (int b = 1; b <= cfg->max_batch; ++b) {
+    rc = build_graph(h, b);
+    if (rc) {
+      mk_destroy(h);
+      return rc;
+    }
+  }
+  // the persistent work-groups poll one another: check that one of them fits
+  // a CU with the largest LDS any schedule asks for
+  size_t lds_need = 0;
+  for (auto& kv : h->graphs) {
+    lds_need = std::max(lds_need, lds_bytes(kv.second.nslot, kv.second.xb));
+    h->part_bytes = std::max(h->part_bytes, part_bytes_of(h, kv.second));
+  }
+  int per_cu = 0;
+  if (step_occupancy(lds_need, &per_cu) != hipSuccess || per_cu < 1) {
+    mk_destroy(h);
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (hipMalloc(&h->d_part, h->part_bytes) != hipSuccess) {
+    mk_destroy(h);
+    return MK_ERR_OOM;
+  }
+  if (hipMemset(h->d_part, 0, h->part_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    mk_destroy(h);
+    return MK_ERR_HIP;
+  }
+  int coop_ok = 0;
+  if (hipDeviceGetAttribute(&coop_ok, hipDeviceAttributeCooperativeLaunch, h->device) != hipSuccess) coop_ok = 0;
+  h->coop = coop_ok && env_int("MK_COOP", 1) != 0;
   *out = h;
   return MK_OK;
 }
@@ -377,16 +417,12 @@ static void free_graph(GraphDev& g) {
   (void)hipFree(g.d_off);
   (void)hipFree(g.d_expect);
   (void)hipFree(g.d_attn_map);
-  (void)hipFree(g.d_part);
   free_plan(&g.plan);
 }
 
-static int get_graph(mk_handle* h, int b, GraphDev** out) {
-  auto it = h->graphs.find(b);
-  if (it != h->graphs.end()) {
-    *out = &it->second;
-    return MK_OK;
-  }
+// Build, validate and upload the schedule of batch size b (mk_create only:
+// the step never allocates or copies on the host side).
+static int build_graph(mk_handle* h, int b) {
   GraphDev g;
   g.nslot = nslot_for(h->lds_max, b, h->mfma_min_batch);
   g.xb = xb_for(h->lds_max, g.nslot);
@@ -397,8 +433,7 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
   bool ok = hipMalloc(&g.d_tasks, sizeof(Task) * (size_t)std::max(1, P.n_tasks)) == hipSuccess &&
             hipMalloc(&g.d_off, sizeof(int) * (h->ncu + 1)) == hipSuccess &&
             hipMalloc(&g.d_expect, sizeof(int) * (size_t)P.n_counters * kShards) == hipSuccess &&
-            hipMalloc(&g.d_attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1)) == hipSuccess &&
-            hipMalloc(&g.d_part, sizeof(float) * 1024 * (size_t)(pc.L + 1) * std::max(1, P.part_blocks)) == hipSuccess;
+            hipMalloc(&g.d_attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1)) == hipSuccess;
   if (!ok) {
     free_graph(g);
     return MK_ERR_OOM;
@@ -406,15 +441,17 @@ static int get_graph(mk_handle* h, int b, GraphDev** out) {
   ok = hipMemcpy(g.d_tasks, P.tasks, sizeof(Task) * P.n_tasks, hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(g.d_off, P.task_off, sizeof(int) * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(g.d_expect, P.expect, sizeof(int) * (size_t)P.n_counters * kShards, hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemcpy(g.d_attn_map, P.attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemset(g.d_part, 0, sizeof(float) * 1024 * (size_t)(pc.L + 1) * std::max(1, P.part_blocks)) == hipSuccess;
+       hipMemcpy(g.d_attn_map, P.attn_map, sizeof(int) * (size_t)pc.L * (h->ncu + 1), hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) {
     free_graph(g);
     return MK_ERR_HIP;
   }
-  auto res = h->graphs.emplace(b, g);
-  *out = &res.first->second;
+  h->graphs.emplace(b, g);
   return MK_OK;
+}
+
+static size_t part_bytes_of(const mk_handle* h, const GraphDev& g) {
+  return sizeof(float) * 1024 * (size_t)(h->cfg.n_layers + 1) * std::max(1, g.plan.part_blocks);
 }
 
 int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
@@ -426,9 +463,9 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   if (!tokens || !positions || !seq_lens || !kv || !kv->k || !kv->v || !logits_out) return MK_ERR_INVALID_ARG;
   if (kv->batch_cap < batch || kv->seq_cap < 1) return MK_ERR_INVALID_ARG;
   if ((long long)h->cfg.n_kv_heads * batch * kv->seq_cap >= (1LL << 31)) return MK_ERR_UNSUPPORTED;
-  GraphDev* g = nullptr;
-  int rc = get_graph(h, batch, &g);
-  if (rc) return rc;
+  auto git = h->graphs.find(batch);
+  if (git == h->graphs.end()) return MK_ERR_INVALID_ARG;  // every batch 1..max_batch is built by mk_create
+  GraphDev* g = &git->second;
   const mk_model_cfg& c = h->cfg;
   DevArgs A;
   memset(&A, 0, sizeof(A));
@@ -474,7 +511,7 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.qkv = h->qkv;
   A.attn_out = h->attn_out;
   A.act = h->act;
-  A.part = g->d_part;
+  A.part = h->d_part;
   A.apart = h->apart;
   A.banks = h->banks;
   A.status = h->status;
@@ -495,7 +532,8 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.trace = h->trace;
   A.trace_cap = h->trace_cap;
   A.attn_pad = h->attn_pad;
-  if (launch_step(A, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  A.dump = h->dump;
+  if (launch_step(A, (hipStream_t)stream, h->coop != 0) != hipSuccess) return MK_ERR_HIP;
   h->rowtag = A.rowtag;
   h->step += 1;
   return MK_OK;
@@ -546,7 +584,10 @@ int mk_get_status(mk_handle* h, void* stream, uint32_t* status) {
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   uint32_t s[2];
   if (hipMemcpy(s, h->status, 8, hipMemcpyDeviceToHost) != hipSuccess) return MK_ERR_HIP;
-  *status = s[0];
+  // word 1 is the kernel's sticky abort flag: once a wait timed out, every
+  // later step gives up its long waits too, so TIMEOUT stays reported until
+  // mk_reset clears the flag
+  *status = s[0] | (s[1] ? MK_STATUS_TIMEOUT : 0u);
   if (s[0] && hipMemset(h->status, 0, 4) != hipSuccess) return MK_ERR_HIP;
   return MK_OK;
 }
@@ -560,16 +601,21 @@ int mk_reset(mk_handle* h, void* stream) {
   bool ok = hipMemset(h->ws, 0, h->tagged_bytes) == hipSuccess &&
             hipMemset(h->banks, 0, (size_t)2 * h->bank_words * 4) == hipSuccess &&
             hipMemset(h->status, 0, 8) == hipSuccess;
-  for (auto& kv : h->graphs)
-    ok = ok && hipMemset(kv.second.d_part, 0,
-                         sizeof(float) * 1024 * (size_t)(h->cfg.n_layers + 1) * std::max(1, kv.second.plan.part_blocks)) == hipSuccess;
+  ok = ok && hipMemset(h->d_part, 0, h->part_bytes) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   return ok ? MK_OK : MK_ERR_HIP;
+}
+
+int mk_set_midstate_dump(mk_handle* h, float* hidden_out) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  h->dump = hidden_out;
+  return MK_OK;
 }
 
 int mk_destroy(mk_handle* h) {
   if (!h) return MK_ERR_INVALID_ARG;
   for (auto& kv : h->graphs) free_graph(kv.second);
+  (void)hipFree(h->d_part);
   (void)hipFree(h->trace);
   (void)hipFree(h->d_layers);
   (void)hipFree(h->ws);

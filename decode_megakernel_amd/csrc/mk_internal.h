@@ -160,6 +160,7 @@ struct DevArgs {
   uint64_t* trace;          // optional per-task timestamps [ncu][trace_cap][4], NULL = off
   int32_t trace_cap;
   int32_t attn_pad;         // attention partition: empty rows ahead of each segment (upper bound)
+  float* dump;              // optional caller buffer [L+1][bcap][d]: residual stream, tag bit cleared (NULL = off)
 };
 
 // Host planner --------------------------------------------------------------

@@ -283,7 +283,8 @@ __device__ __noinline__ bool spin_fail(const uint32_t* status, Ctrl* c) {
 // returns false when the wait must be abandoned
 __device__ __forceinline__ bool spin_ok(DArgs A, Ctrl* c, Spin& sp) {
   if (lds_aborted(c)) return false;
-  if ((++sp.it & 63) == 0) {
+  // a zero time limit (a host-forced timeout) gives up at the first failed poll
+  if ((++sp.it & 63) == 0 || A->timeout_ticks == 0) {
     if (spin_fail(A->status, c)) return false;
     if (now_ticks() - sp.t0 > A->timeout_ticks) {
       atomicOr(A->status, kStatusTimeout);
@@ -303,7 +304,8 @@ __device__ __forceinline__ bool spin_ok(DArgs A, Ctrl* c, Spin& sp) {
 #endif
 __device__ __forceinline__ bool poll_ok(DArgs A, Ctrl* c, Spin& sp) {
   if (lds_aborted(c)) return false;
-  if ((++sp.it & 63) == 0) {
+  // a zero time limit (a host-forced timeout) gives up at the first failed poll
+  if ((++sp.it & 63) == 0 || A->timeout_ticks == 0) {
     if (spin_fail(A->status, c)) return false;
     if (now_ticks() - sp.t0 > A->timeout_ticks) {
       atomicOr(A->status, kStatusTimeout);
@@ -718,7 +720,7 @@ __device__ __forceinline__ bool loader_wait_free(DArgs A, Ctrl* c, int slot, int
     __builtin_amdgcn_s_sleep(1);
     if (lds_flag_read(&c->freed[slot]) >= need) break;
     if (lds_flag_read(&c->abort)) return false;
-    if ((it & 255) == 255 && now_ticks() - t0 > A->timeout_ticks) {
+    if (((it & 255) == 255 || A->timeout_ticks == 0) && now_ticks() - t0 > A->timeout_ticks) {
       atomicOr(A->status, kStatusTimeout);
       __hip_atomic_store(A->status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       lds_flag_write(&c->abort, 1);
@@ -1181,6 +1183,7 @@ struct EpiCtx {
   float* out;    // QKV: qkv rows; O: mid-layer residual; DOWN: next residual; GU: SiLU·up; LM: logits
   float* xo;     // O / DOWN: the next RMSNorm's input
   float* ssout;  // O / DOWN: its per-16-row sums of squares
+  float* dump;   // DOWN: the caller's mid-state dump of this layer's output (NULL = none)
 };
 __device__ __forceinline__ EpiCtx make_epi(DArgs A, const Task& t) {
   EpiCtx e;
@@ -1190,7 +1193,7 @@ __device__ __forceinline__ EpiCtx make_epi(DArgs A, const Task& t) {
   e.b = A->b;
   e.bcap = A->bcap;
   e.tags = A->rowtag;
-  e.xo = e.ssout = nullptr;
+  e.xo = e.ssout = e.dump = nullptr;
   switch (t.stage) {
     case ST_QKV:
       e.out = A->qkv + (size_t)l * A->bcap * A->nqkv;
@@ -1206,6 +1209,7 @@ __device__ __forceinline__ EpiCtx make_epi(DArgs A, const Task& t) {
       e.out = A->hres + (size_t)(l + 1) * A->bcap * A->d;
       e.xo = A->xattn + (size_t)(l + 1) * A->bcap * A->d;
       e.ssout = A->ssattn + (size_t)(l + 1) * (A->d / 16) * A->bcap;
+      e.dump = A->dump ? A->dump + (size_t)(l + 1) * A->bcap * A->d : nullptr;
       e.ostride = A->d;
       break;
     case ST_GU:
@@ -1243,6 +1247,8 @@ __device__ __forceinline__ void gemv_epilogue(const EpiCtx& e, Ctrl* c, int lr, 
       if (valid) {
         co_store_tag(e.out, off, h, tg);
         co_store_tag(e.xo, off, xn, tg);
+        // the mid-state dump holds the value consumers use (tag bit cleared)
+        if (e.dump) e.dump[(size_t)n * e.ostride + lr] = untagf(h);
       }
       float ss = sum16(h * h);
       if (valid && row == 0) co_store_tag(e.ssout, (uint32_t)((((size_t)lr >> 4) * e.bcap + n) * 4), ss, tg);
@@ -1684,6 +1690,7 @@ __device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int la
     const uint16_t* nw = as_const(A->layers)[0].attn_norm + col;
     co_store16(A->hres, (uint32_t)(((size_t)n * A->d + col) * 4),
                u32x4{tagged(h[0], tg), tagged(h[1], tg), tagged(h[2], tg), tagged(h[3], tg)});
+    if (A->dump) *(f32x4*)(A->dump + (size_t)n * A->d + col) = f32x4{h[0], h[1], h[2], h[3]};
     co_store16(A->xattn, (uint32_t)(((size_t)n * A->d + col) * 4),
                u32x4{tagged(h[0] * bf2f(nw[0]), tg), tagged(h[1] * bf2f(nw[1]), tg),
                      tagged(h[2] * bf2f(nw[2]), tg), tagged(h[3] * bf2f(nw[3]), tg)});
@@ -2460,13 +2467,35 @@ size_t lds_bytes(int nslot, int xb_bytes) {
   return (size_t)nslot * kChunkBytes + xb_bytes + kRedBytes + kCtrlBytes;
 }
 
-hipError_t launch_step(const DevArgs& A, hipStream_t stream) {
-  const size_t lds = lds_bytes(A.nslot, A.xb_bytes);
+static hipError_t set_lds_limit(size_t lds) {
   static size_t lds_set = 0;
   if (lds > lds_set) {
     hipError_t e = hipFuncSetAttribute((const void*)mk_step_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_set = lds;
+  }
+  return hipSuccess;
+}
+
+// Work-groups of the step kernel that fit one CU at the given dynamic LDS
+// size (0 when they do not fit at all).
+hipError_t step_occupancy(size_t lds, int* blocks_per_cu) {
+  hipError_t e = set_lds_limit(lds);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_step_kernel, kThreads, lds);
+}
+
+// One launch of ncu persistent work-groups.  The work-groups poll each other,
+// so all of them must be resident at once: a cooperative launch has the
+// runtime guarantee that (it fails rather than start a partial grid).
+hipError_t launch_step(const DevArgs& A, hipStream_t stream, bool coop) {
+  const size_t lds = lds_bytes(A.nslot, A.xb_bytes);
+  hipError_t e = set_lds_limit(lds);
+  if (e != hipSuccess) return e;
+  if (coop) {
+    void* args[] = {(void*)&A};
+    return hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(A.ncu), dim3(kThreads), args, (unsigned)lds,
+                                      stream);
   }
   hipLaunchKernelGGL(mk_step_kernel, dim3(A.ncu), dim3(kThreads), lds, stream, A);
   return hipGetLastError();

@@ -46,7 +46,8 @@ extern "C" {
 #define MK_STATUS_BAD_POSITION 2u  /* positions[i] outside [0, min(max_seq, seq_cap)) */
 #define MK_STATUS_BAD_SEQLEN 4u    /* seq_lens[i] != positions[i] + 1               */
 #define MK_STATUS_TIMEOUT 8u       /* a dependency wait exceeded the spin limit; the
-                                      step was abandoned and the handle needs mk_reset */
+                                      step was abandoned, later steps give up their waits
+                                      too, and this bit stays reported until mk_reset */
 
 typedef struct mk_handle mk_handle;   /* opaque, owned by the library */
 
@@ -98,17 +99,34 @@ typedef struct {
   int32_t seq_cap;
 } mk_kv_cache;
 
-/* Create a handle: validates the shape (MK_ERR_UNSUPPORTED also when
- * n_kv_heads x max_batch x max_seq reaches 2^31), allocates the library-owned
- * workspace (per-layer activations, partial sums, counters, RoPE table) on
- * the current HIP device.  *out is set only on success. */
+/* Create a handle.  The model dimensions are runtime values, so one library
+ * serves every shape (the ForgeMegakernel summary, "Compiled megakernels": a
+ * megakernel compiler whose constants derive from model dimensions loses
+ * utilization as the model shrinks).  Validates the shape
+ * (MK_ERR_UNSUPPORTED also when n_kv_heads x max_batch x max_seq reaches 2^31,
+ * or when one persistent work-group does not fit a compute unit), allocates
+ * the library-owned workspace (per-layer activations, partial sums, counters,
+ * RoPE table) on the current HIP device, and builds, validates and uploads
+ * the per-CU instruction streams of every batch size 1..max_batch (the
+ * per-SM instruction streams of "4.1 The universal knowledge base and the
+ * milestones"; the task descriptors of the Cohere engine digest).  It
+ * synchronises the device.  *out is set only on success; on failure nothing
+ * stays allocated.  Setting MK_COOP=0 in the environment switches the step
+ * launches from cooperative to plain ones (then no other kernel may run on
+ * the device during a step: the work-groups wait for one another). */
 int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out);
 
-/* One greedy decode step for sequences 0..batch-1 (cache rows 0..batch-1),
- * enqueued on `stream` as one kernel launch; returns without synchronising.
+/* One greedy decode step (the ForgeMegakernel summary, "2.1 The decode
+ * step") for sequences 0..batch-1 (cache rows 0..batch-1), enqueued on
+ * `stream` as ONE kernel launch ("2.3 Megakernels": the step stays within one
+ * host launch); the call never allocates, copies or synchronises on the host,
+ * also when the batch size differs from the previous step's (a sequence
+ * joining: "3.1 Limited performance across cells", the ninth sequence).
  *   tokens[batch]     device int32: the token each sequence feeds now;
  *   positions[batch]  device int32: its decode position p_i; the new K/V row
- *                     is written to cache slot p_i and RoPE uses p_i;
+ *                     is written to cache slot p_i and RoPE uses p_i (each
+ *                     sequence its own: "3.2 Unverifiable correctness of
+ *                     kernel fusing", the broadcast-position bug);
  *   seq_lens[batch]   device int32: rows attended after the write, must be
  *                     p_i + 1 (checked on the device);
  *   logits_out        device float [batch][vocab], written;
@@ -125,7 +143,9 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
                    const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
                    int32_t* next_tokens_out, void* stream);
 
-/* Copy the residual stream of the last step, enqueued on `stream`:
+/* Copy the residual stream of the last step, enqueued on `stream` (the
+ * per-layer hidden states the mid-state oracle checks: the ForgeMegakernel
+ * summary, "4.2 The mid-state test oracle"):
  * dst [n_layers+1][batch][hidden] float, entry l = input of layer l (entry 0
  * is the gathered embedding, entry n_layers leaves the last layer).  The
  * kernel hands activations between compute units with a step tag in each
@@ -134,7 +154,8 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
  * bf16 embedding rows come back exactly). */
 int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream);
 
-/* Copy one per-layer mid-state buffer of the last step, enqueued on
+/* Copy one per-layer mid-state buffer of the last step ("4.2 The mid-state
+ * test oracle": intermediate states against float64 references), enqueued on
  * `stream`, for sequences 0..batch-1 of every layer, into dst (layout
  * [layers][batch][width], dtype as listed; tag bit cleared as above):
  *   MK_STATE_HIDDEN   float, L+1 layers, width hidden (same as mk_copy_hidden)
@@ -150,7 +171,9 @@ int mk_copy_hidden(mk_handle* h, int32_t batch, float* dst, void* stream);
 #define MK_STATE_ACT 4
 int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* stream);
 
-/* In-kernel trace (enabled when the environment variable MK_TRACE=<n> is set
+/* In-kernel trace: where each compute unit waits (the ForgeMegakernel
+ * summary, "5.2 Kernel experiment", its per-token breakdown: a megakernel's
+ * synchronisation waits sit at its dependency points).  Enabled when the environment variable MK_TRACE=<n> is set
  * at mk_create; otherwise *cap = 0 and nothing is copied).  Copies, enqueued
  * on `stream`, the trace of the last step into dst (device memory of at
  * least (n_cu*cap*4 + n_cu*80)*8 bytes): for each CU and each of its first
@@ -175,20 +198,41 @@ int mk_copy_state(mk_handle* h, int32_t which, int32_t batch, void* dst, void* s
 int mk_copy_trace(mk_handle* h, void* dst, int64_t bytes, int32_t* n_cu, int32_t* cap, void* stream);
 
 /* Synchronise `stream`, return the device status bits accumulated since the
- * last call in *status and clear them. */
+ * last call in *status and clear them, except MK_STATUS_TIMEOUT, which stays
+ * set until mk_reset.  The checks behind the bits are the kernel's own input
+ * validation (tokens, positions, lengths) and its bounded waits (the static
+ * deadlock-freedom of the AutoMegaKernel page's schedule validator is checked
+ * on the host when the schedules are built; the bound makes a wait that never
+ * ends a reported error instead of a hang). */
 int mk_get_status(mk_handle* h, void* stream, uint32_t* status);
 
 /* Synchronise `stream` and clear all counters, status and the step tags of
- * the library-owned activations (needed after a MK_STATUS_TIMEOUT). */
+ * the library-owned activations (needed after a MK_STATUS_TIMEOUT).  The
+ * decode state itself (KV cache, positions) is the caller's, so resuming is
+ * calling mk_decode_step again with the same buffers. */
 int mk_reset(mk_handle* h, void* stream);
 
-/* Free library-owned memory.  The caller's weights and caches are untouched. */
+/* Mid-state dump: while set, every step also writes its residual stream
+ * (the values mk_copy_hidden returns) into hidden_out, a DEVICE buffer the
+ * caller owns, layout [n_layers+1][max_batch][hidden] float (entry l = input
+ * of layer l, sequence n at row n).  The stores are the kernel's own
+ * residual-stream stores with a second base pointer, inside the same launch
+ * ("4.2 The mid-state test oracle": intermediate states read against float64
+ * references).  NULL switches it off.  The buffer must stay valid for every
+ * step enqueued while it is set. */
+int mk_set_midstate_dump(mk_handle* h, float* hidden_out);
+
+/* Free library-owned memory (workspace, schedules, trace).  The caller's
+ * weights and caches are untouched. */
 int mk_destroy(mk_handle* h);
 
+/* Name of an MK_* return code (static string). */
 const char* mk_error_string(int code);
 
 /* Schedule inspection, host only (no GPU needed): build and validate the
- * per-CU instruction streams for `batch` on `n_cu` compute units. */
+ * per-CU instruction streams for `batch` on `n_cu` compute units (the same
+ * builder mk_create uses) and report their shape and byte balance (the Cohere
+ * engine digest: wave quantisation and backfilling idle SMs). */
 typedef struct {
   int32_t n_tasks;
   int32_t max_tasks_per_cu;

@@ -108,6 +108,30 @@ def kv_capacity(max_context: int, steps: int, align: int = 256) -> int:
     return ((need + align - 1) // align) * align
 
 
+def make_kv_layer(shape: ModelShape, seed: int, contexts, batch_cap: int, seq_cap: int, layer: int,
+                  device="cpu"):
+    """Layer `layer` of the K and V caches: bf16 [batch_cap][n_kv][seq_cap][head_dim].
+
+    The same bits make_kv_cache stores for that layer (one generator per
+    layer and tensor), so any layer can be regenerated alone: positions <
+    contexts[i] of row i are N(0,1) in bf16, every other slot the NaN
+    sentinel."""
+    nkv, hd = shape.n_kv_heads, shape.head_dim
+    pos = torch.arange(seq_cap, device=device)
+    ctx = torch.zeros(batch_cap, dtype=torch.long, device=device)
+    ctx[: len(contexts)] = torch.tensor(list(contexts), dtype=torch.long, device=device)
+    valid = (pos[None, :] < ctx[:, None])[:, None, :, None]  # [B,1,S,1]
+    nan = torch.tensor(BF16_NAN_SENTINEL, dtype=torch.int16, device=device).view(torch.bfloat16)
+    out = []
+    for tag in ("k", "v"):
+        g = _generator(seed, f"kv.{layer}.{tag}", device)
+        x = torch.randn((batch_cap, nkv, seq_cap, hd), generator=g,
+                        dtype=torch.float32, device=device).to(torch.bfloat16)
+        out.append(torch.where(valid, x, nan))
+        del x
+    return out[0], out[1]
+
+
 def make_kv_cache(shape: ModelShape, seed: int, contexts, batch_cap: int, seq_cap: int,
                   device="cpu"):
     """K and V caches, bf16, layout [L][batch_cap][n_kv][seq_cap][head_dim].
@@ -119,18 +143,8 @@ def make_kv_cache(shape: ModelShape, seed: int, contexts, batch_cap: int, seq_ca
     L, nkv, hd = shape.n_layers, shape.n_kv_heads, shape.head_dim
     K = torch.empty((L, batch_cap, nkv, seq_cap, hd), dtype=torch.bfloat16, device=device)
     V = torch.empty_like(K)
-    pos = torch.arange(seq_cap, device=device)
-    ctx = torch.zeros(batch_cap, dtype=torch.long, device=device)
-    ctx[: len(contexts)] = torch.tensor(list(contexts), dtype=torch.long, device=device)
-    valid = (pos[None, :] < ctx[:, None])[:, None, :, None]  # [B,1,S,1]
-    nan = torch.tensor(BF16_NAN_SENTINEL, dtype=torch.int16, device=device).view(torch.bfloat16)
     for l in range(L):
-        for tgt, tag in ((K, "k"), (V, "v")):
-            g = _generator(seed, f"kv.{l}.{tag}", device)
-            x = torch.randn((batch_cap, nkv, seq_cap, hd), generator=g,
-                            dtype=torch.float32, device=device).to(torch.bfloat16)
-            tgt[l] = torch.where(valid, x, nan)
-            del x
+        K[l], V[l] = make_kv_layer(shape, seed, contexts, batch_cap, seq_cap, l, device)
     return K, V
 
 
