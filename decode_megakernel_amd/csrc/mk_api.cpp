@@ -129,11 +129,13 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
   p.gemv_mode = env_int("MK_GEMV_MODE", 0);
   p.skip_prev = env_int("MK_PLAN_SKIP_PREV", 2);
   p.attn_idle = env_int("MK_ATTN_IDLE", 1);
+  p.ksplit = env_int("MK_KSPLIT", 1);
+  p.ksplit_min_windows = env_int("MK_KSPLIT_MIN_WINDOWS", 5);
   return p;
 }
 
 static int xb_for(int lds_max, int nslot) {
-  long long xb = (long long)lds_max - (long long)nslot * kChunkBytes - kRedBytes - kCtrlBytes;
+  long long xb = (long long)lds_max - (long long)nslot * kSlotBytes - kRedBytes - kCtrlBytes;
   xb &= ~255LL;
   return (int)xb;
 }
@@ -177,6 +179,7 @@ int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats*
     out->stage_tasks[i] = P.stage_tasks[i];
     out->stage_ksplit[i] = P.stage_ksplit[i];
     out->stage_rows_per_task[i] = P.stage_rows[i];
+    out->stage_kpieces[i] = P.stage_kpieces[i];
   }
   // placement of one layer: which CUs run each stage
   {

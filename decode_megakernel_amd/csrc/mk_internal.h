@@ -18,8 +18,14 @@ constexpr int kComputeWaves = 4;
 constexpr int kLoaderWaves = 3;
 constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
 constexpr int kComputeThreads = 64 * kComputeWaves;
-constexpr int kChunkBytes = 16384;          // one LDS ring slot
+constexpr int kChunkBytes = 16384;          // data of one streamed chunk (16 rows x 512 bf16, or 32/64 K+V rows)
 constexpr int kWaveLoads = kChunkBytes / 1024;  // 16 B per lane x 64 lanes per wave-load
+// LDS ring slot: a GEMV chunk's 16 weight rows sit kRowPitch bytes apart (1 KB
+// of data + 16 B of padding), so the 16 rows an MFMA A operand reads at one
+// K offset fall in different LDS banks while every row still arrives as one
+// contiguous 1 KB load
+constexpr int kRowPitch = 1040;
+constexpr int kSlotBytes = 16 * kRowPitch;
 constexpr int kMaxSlots = 8;
 constexpr int kShards = 64;                  // dependency counters are sharded 64 ways
 constexpr int kMaxBatch = 16;
@@ -48,23 +54,26 @@ constexpr int kStatWords = 80;               // trace: per-CU phase totals (uint
 constexpr int kCtrlBytes = MK_PHASE_TRACE ? 1536 : 1024;             // LDS control block (ring flags, per-wave state, sequence inputs)
 
 enum Stage : int32_t { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_LM = 5, ST_EMBED = 6 };
-enum TaskType : int32_t { TT_EMBED = 1, TT_GEMV = 2, TT_ATTN = 3 };
+enum TaskType : int32_t { TT_EMBED = 1, TT_GEMV = 2, TT_ATTN = 3, TT_FIN = 4 };
 
 // One instruction of a CU's stream (64 bytes).
 struct Task {
   int32_t type;
   int32_t stage;
   int32_t layer;
-  int32_t row0;        // GEMV: first logical output row; EMBED: first column
+  int32_t row0;        // GEMV / FIN: first logical output row; EMBED: first column
   int32_t nsub;        // GEMV: 16-row sub-tiles of the task (1..4*tiles_per_wave); EMBED: number of columns
   int32_t k0, k1;      // GEMV: K range, k0 a multiple of 512
   int32_t ks, nks;     // GEMV: this task's piece index among the nks pieces that split the group's K
   int32_t group;       // GEMV: row group (counter index within the stage when nks > 1)
-  int32_t part_slot;   // GEMV nks > 1: partial block of piece 0 of the group (piece k at part_slot + k)
+  int32_t part_slot;   // GEMV nks > 1: partial block of piece 0 of the group (piece k at part_slot + k);
+                       // K-split stage (GEMV publish / FIN): first 256-float tile slot of the stage,
+                       // sub-tile u's piece k at part_slot + u * nks + k
   int32_t wait_ctr;    // dependency counter to wait on, -1 = none
   int32_t signal_ctr;  // counter this task signals when its outputs are complete
   int32_t nchunks;     // GEMV: LDS chunks streamed by the loader (nsub x k-blocks)
-  int32_t flags;       // bit 0: signal signal_ctr after this task (the CU's last task of the stage)
+  int32_t flags;       // kTaskSignal: signal signal_ctr after this task (the CU's last task of the stage);
+                       // kTaskPublish: K-split piece, publishes every owned sub-tile's partial tile
   int32_t pad;
 };
 static_assert(sizeof(Task) == 64, "Task must be 64 bytes");
@@ -171,10 +180,13 @@ struct PlanCfg {
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
   int gemv_mode = 0;    // 0: cheaper of row-owner / stream-K per stage, 1: row-owner, 2: stream-K
   int attn_idle = 1;    // attention prefers the CUs its layer's QKV stage left idle
+  int ksplit = 1;       // K-split stages whose tasks would need many LDS input windows
+  int ksplit_min_windows = 5;  // ... at least this many (per task of the tiling it replaces)
   int skip_prev = 2;    // row-owner stages skip the CUs of a previous stage that left CUs idle
                         // when the tiles per CU grow by at most skip_prev - 1 (0: never)
 };
 constexpr int kTaskSignal = 1;
+constexpr int kTaskPublish = 2;
 
 struct Plan {
   int batch = 0;
@@ -189,6 +201,7 @@ struct Plan {
   int stage_ksplit[6] = {0, 0, 0, 0, 0, 0};
   int stage_rows[6] = {0, 0, 0, 0, 0, 0};
   int stage_owner[6] = {0, 0, 0, 0, 0, 0};  // 1: whole sub-tiles per CU over full K (no split)
+  int stage_kpieces[6] = {0, 0, 0, 0, 0, 0};  // K-split stages: K pieces (one LDS window each), else 0
   long long weight_bytes = 0;
   long long max_cu_weight_bytes = 0;
   double balance_min = 1.0;

@@ -233,7 +233,7 @@ static_assert(sizeof(Ctrl) <= kCtrlBytes, "control block exceeds its LDS budget"
 // reduction scratch, control block.  Every role derives its pointers from
 // this array so that LDS accesses compile to ds_* instructions.
 extern __shared__ __attribute__((aligned(16))) char mk_lds[];
-__device__ __forceinline__ char* xb_stage(DArgs A) { return mk_lds + (size_t)A->nslot * kChunkBytes; }
+__device__ __forceinline__ char* xb_stage(DArgs A) { return mk_lds + (size_t)A->nslot * kSlotBytes; }
 __device__ __forceinline__ float* red_scratch(DArgs A) { return (float*)(xb_stage(A) + A->xb_bytes); }
 __device__ __forceinline__ Ctrl* ctrl_block(DArgs A) { return (Ctrl*)((char*)red_scratch(A) + kRedBytes); }
 
@@ -674,27 +674,17 @@ __device__ __forceinline__ RowBase sub_rows(DArgs A, const Task& t, int sub) {
   return rb;
 }
 
-// One GEMV chunk: 16 rows x 512 K (VALU: wave-load j = row j) or 16 MFMA
-// k-steps of 16 rows x 32 K in the A-operand lane layout.
+// One GEMV chunk: 16 rows x 512 K, wave-load j = row j's 1 KB, contiguous in
+// HBM and kRowPitch bytes apart in LDS (both the VALU and the MFMA tiles read
+// this layout; a load that gathers 16 rows x 64 B per instruction instead
+// streamed about 27% slower).
 __device__ __forceinline__ void dma_gemv_chunk(DArgs A, const RowBase& rb, int kb, int k1, int lane, char* dst) {
-  if (!A->mfma) {
-    const int kk = kb * kKBlock + 8 * lane;
-    const bool kok = kk < k1;
+  const int kk = kb * kKBlock + 8 * lane;
+  const bool kok = kk < k1;
 #pragma unroll
-    for (int j = 0; j < kWaveLoads; ++j) {
-      const uint16_t* src = (j < 8 ? rb.b0 : rb.b1) + (size_t)(j & 7) * rb.stride + kk;
-      dma16((kok && j < rb.nrows) ? (const void*)src : (const void*)A->zero, dst + j * 1024);
-    }
-  } else {
-    const int row = lane & 15;
-    const uint16_t* rp = (row < 8 ? rb.b0 : rb.b1) + (size_t)(row & 7) * rb.stride;
-    const bool rok = row < rb.nrows;
-    const int kk0 = kb * kKBlock + 8 * (lane >> 4);
-#pragma unroll
-    for (int j = 0; j < kWaveLoads; ++j) {
-      const int kk = kk0 + 32 * j;
-      dma16((rok && kk < k1) ? (const void*)(rp + kk) : (const void*)A->zero, dst + j * 1024);
-    }
+  for (int j = 0; j < kWaveLoads; ++j) {
+    const uint16_t* src = (j < 8 ? rb.b0 : rb.b1) + (size_t)(j & 7) * rb.stride + kk;
+    dma16((kok && j < rb.nrows) ? (const void*)src : (const void*)A->zero, dst + j * kRowPitch);
   }
 }
 
@@ -791,7 +781,7 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
         RowBase rb = sub_rows(A, t, sub);
         while (local < nch) {
           if (!ring_acquire(A, c, R, lane)) return;
-          dma_gemv_chunk(A, rb, kb, t.k1, lane, ring + (size_t)R.slot * kChunkBytes);
+          dma_gemv_chunk(A, rb, kb, t.k1, lane, ring + (size_t)R.slot * kSlotBytes);
           ring_issued(A, c, R, lane);
           local += kLoaderWaves;
           const int old_sub = sub;
@@ -819,7 +809,7 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
           if (!ring_acquire(A, c, R, lane)) return;
           const size_t row0 = (head + P.j0 + (size_t)ch * rpc) * A->hd;
           const int rows = min(rpc, P.ncached - ch * rpc);
-          char* dst = ring + (size_t)R.slot * kChunkBytes;
+          char* dst = ring + (size_t)R.slot * kSlotBytes;
           if (A->hd == 128) dma_attn_chunk<128>(A, A->kc + row0, A->vc + row0, rows, lane, dst);
           else dma_attn_chunk<64>(A, A->kc + row0, A->vc + row0, rows, lane, dst);
           ring_issued(A, c, R, lane);
@@ -966,7 +956,7 @@ __device__ __forceinline__ bool poll_ss(DArgs A, Ctrl* c, const float* ss, int n
 //      normalize their input.  Skipped when the same slice is already staged.
 //      The input words are polled until they carry the step tag.
 __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int kk1, char* xb, Ctrl* c, CState& s, int w,
-                            int lane) {
+                            int lane, bool want_rms = true) {
   if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == kk0 && s.x_k1 == kk1) return true;
   // analysis builds: sub-phases of the QKV staging (compute wave 0)
   uint64_t* sp = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0 && t.stage == ST_QKV) ? MK_PSTAT(c, 36) : nullptr;
@@ -994,7 +984,7 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   const uint32_t tags = A->rowtag;
   // RMS partial sums of sequence w, first attempt in flight with the input
   const float* ss = stage_ss(A, t.stage, t.layer);
-  const bool rms = ss && !(s.r_stage == t.stage && s.r_layer == t.layer);
+  const bool rms = want_rms && ss && !(s.r_stage == t.stage && s.r_layer == t.layer);
   const int nt = A->d / 16;
   const uint32_t tw = (tags >> w) & 1u;
   uint32_t ssu[kSsLoads];
@@ -1086,7 +1076,7 @@ __device__ __forceinline__ void valu_chunk(const char* slot, const char* xb, int
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    u32x4 wv = lds_ld16(slot + j * 1024 + lane * 16);
+    u32x4 wv = lds_ld16(slot + j * kRowPitch + lane * 16);
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[j][n] = dot8_bf16(wv, xh[n], dot8_bf16(wv, xl[n], acc[j][n]));
   }
@@ -1140,7 +1130,8 @@ __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int
   const int n = min(lane & 15, b - 1), kq = 8 * (lane >> 4);
   const char* xh = xb + ((size_t)n * ksp + kl + kq) * 2;
   const char* xl = xh + xlo_off;
-  const char* wv = slot + lane * 16;
+  // A operand of k-step s: row lane & 15, K elements 32 s + 8 (lane >> 4) .. + 7
+  const char* wv = slot + (lane & 15) * kRowPitch + (lane >> 4) * 16;
   f32x4 alo = {0.f, 0.f, 0.f, 0.f};  // the lo halves accumulate separately (two independent MFMA chains)
   if (kl + kKBlock <= klen) {
     // whole 512-wide block: LDS reads four K-steps at a time ahead of their MFMAs
@@ -1149,7 +1140,7 @@ __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int
       u32x4 bh[4], bl[4], av[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        av[u] = lds_ld16(wv + (s0 + u) * 1024);
+        av[u] = lds_ld16(wv + (s0 + u) * 64);
         bh[u] = lds_ld16(xh + (s0 + u) * 64);
         bl[u] = lds_ld16(xl + (s0 + u) * 64);
       }
@@ -1164,7 +1155,7 @@ __device__ __forceinline__ void mfma_chunk(const char* slot, const char* xb, int
   } else {
     // the ragged last block of K: steps of 32 up to klen (klen - kl is a multiple of 32)
     for (int s = 0; s < kWaveLoads && kl + 32 * s < klen; ++s) {
-      const u32x4 av = lds_ld16(wv + s * 1024), bh = lds_ld16(xh + s * 64), bl = lds_ld16(xl + s * 64);
+      const u32x4 av = lds_ld16(wv + s * 64), bh = lds_ld16(xh + s * 64), bl = lds_ld16(xl + s * 64);
       alo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bl), alo,
                                                     0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bh), acc,
@@ -1304,7 +1295,9 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   const int M = stage_M(A, t.stage);
   const int nkb = (t.k1 - t.k0 + kKBlock - 1) / kKBlock;
   const int row = lane & 15;
-  const bool has_resid = t.stage == ST_O || t.stage == ST_DOWN;
+  // a K-split piece publishes its partial tiles; the stage's finish tasks run the epilogue
+  const bool publish = (t.flags & kTaskPublish) != 0;
+  const bool has_resid = !publish && (t.stage == ST_O || t.stage == ST_DOWN);
   const float* hin = t.stage == ST_DOWN ? A->hmid + (size_t)t.layer * A->bcap * A->d
                                         : A->hres + (size_t)t.layer * A->bcap * A->d;
   auto tile_row0 = [&](int i) { return t.row0 + 16 * (msub + kComputeWaves * i); };
@@ -1361,7 +1354,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     const int we = min(nkb, wb + wkb);
     const int kk0 = t.k0 + wb * kKBlock, kk1 = min(t.k1, t.k0 + we * kKBlock);
     const uint64_t ts0 = A->trace ? now_ticks() : 0;
-    if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane)) return false;
+    if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane, !publish)) return false;
     if (A->trace) s.t_stage += now_ticks() - ts0;
     gmark(0);
     const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0, xlo_off = A->b * ksp * 2;
@@ -1375,7 +1368,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
           if (i >= nown) break;
           const int gq = s.q + kb * nsub + msub + kComputeWaves * i;
           if (!wait_chunk(A, c, gq, s.w_empty)) return false;
-          const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
+          const char* slot = ring + (size_t)(gq % A->nslot) * kSlotBytes;
           const uint64_t tm0 = A->trace ? now_ticks() : 0;
           valu_chunk<NB>(slot, xb, xlo_off, ksp, kl + 8 * lane, klen, lane, vacc[i]);
           free_chunk(A, c, gq, lane);
@@ -1391,7 +1384,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
           if (i >= nown) return false;
           const int gq = s.q + kb * nsub + msub + kComputeWaves * i;
           if (!wait_chunk(A, c, gq, s.w_empty)) return ok = false;
-          const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
+          const char* slot = ring + (size_t)(gq % A->nslot) * kSlotBytes;
           const uint64_t tm0 = A->trace ? now_ticks() : 0;
           mfma_chunk(slot, xb, xlo_off, ksp, kl, klen, A->b, lane, macc[i]);
           free_chunk(A, c, gq, lane);
@@ -1526,7 +1519,23 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     }
   };
   const int nepi = lead ? nown : 0;  // owned sub-tiles whose epilogue this wave runs
-  if (t.nks > 1) {
+  if (publish) {
+    // K-split piece ks of nks: every owned sub-tile's partial tile goes to its
+    // slot (sub-tile u, piece ks) with the lowest bit of every word set (the
+    // finisher's validity flag), lane-major: lane l's 16 bytes are its values
+    // for (row l & 15, sequences l / 16 + 4 j)
+    float* const pbase = A->part + (size_t)t.layer * A->part_blocks * 1024;
+    static_for<TPW>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (i >= nepi) return false;
+      float val[4], up[4];
+      owned_values(i, val, up);
+      const int u = t.row0 / 16 + msub + kComputeWaves * i;
+      const uint32_t off = (uint32_t)((((uint32_t)t.part_slot + (uint32_t)u * t.nks + t.ks) * 256u + 4u * lane) * 4u);
+      co_store16(pbase, off, u32x4{tagged(val[0], 1u), tagged(val[1], 1u), tagged(val[2], 1u), tagged(val[3], 1u)});
+      return true;
+    });
+  } else if (t.nks > 1) {
     // split K over nks pieces on consecutive CUs (one sub-tile per leading
     // wave, nsub <= 4).  Pieces 1.. publish their partial tiles into this
     // layer's slots with the lowest bit of every word set; piece 0 polls the
@@ -1669,6 +1678,144 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   }
 #endif
   if (A->trace) s.t_epi += now_ticks() - te0;
+  return true;
+}
+
+// ---- K-split finish: for this CU's share of a K-split stage's sub-tiles,
+//      poll the nks published pieces of each sub-tile, sum them in piece
+//      order (a fixed order, so results do not depend on timing), clear the
+//      slots (their only reader; the next write is a step later) and run the
+//      stage's epilogue on the sums.  Compute wave w takes sub-tiles w, w+4, ...
+constexpr int kFinBatch = 8;  // pieces polled per batch, every load in flight
+__device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane) {
+  A = uni(A);
+  Ctrl* c = ctrl_block(A);
+  CState& s = c->cs[w];
+  const Task t = load_task(uni(tp));
+  const int M = stage_M(A, t.stage);
+  const int row = lane & 15;
+  const uint32_t tags = A->rowtag;
+  // every compute wave is done with the previous task's LDS before the RMS
+  // scales are rewritten
+  if (!s.synced && !cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  s.synced = 0;
+  const float* ss = stage_ss(A, t.stage, t.layer);
+  if (ss && !(s.r_stage == t.stage && s.r_layer == t.layer)) {
+    const int nt = A->d / 16;
+    for (int n = w; n < A->b; n += kComputeWaves) {
+      uint32_t ssu[kSsLoads];
+      if (!poll_ss(A, c, ss, n, nt, (tags >> n) & 1u, lane, ssu, false)) return false;
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < kSsLoads; ++k) acc += lane + 64 * k < nt ? __uint_as_float(untag(ssu[k])) : 0.f;
+      acc = group_sum<16>(acc);
+      acc = swap16_sum(acc, acc);
+      acc = swap32_sum(acc, acc);
+      if (lane == 0) c->rms[n] = 1.0f / sqrtf(acc / (float)A->d + A->eps);
+    }
+    s.r_stage = t.stage;
+    s.r_layer = t.layer;
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  }
+  const EpiCtx epi = make_epi(A, t);
+  float rmsv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = (lane >> 4) + 4 * j;
+    rmsv[j] = n < kMaxBatch ? c->rms[n] : 0.f;
+  }
+  const bool has_resid = t.stage == ST_O || t.stage == ST_DOWN;
+  const bool gu = t.stage == ST_GU;
+  const float* hin = t.stage == ST_DOWN ? A->hmid + (size_t)t.layer * A->bcap * A->d
+                                        : A->hres + (size_t)t.layer * A->bcap * A->d;
+  const uint16_t* nwp = nullptr;
+  if (t.stage == ST_O) nwp = as_const(A->layers)[t.layer].mlp_norm;
+  if (t.stage == ST_DOWN) nwp = t.layer + 1 < A->L ? as_const(A->layers)[t.layer + 1].attn_norm : A->final_norm;
+  float* const pbase = A->part + (size_t)t.layer * A->part_blocks * 1024;
+  const int nks = t.nks;
+  for (int k = w; k < t.nsub; k += kComputeWaves) {
+    const int u = t.row0 / 16 + k;
+    const int lr = 16 * u + row;
+    // the piece values of this lane (rows lane & 15) and, for gate/up, of
+    // lane ^ 8 (a gate row's up row is 8 rows further in the tile)
+    const uint32_t slot0 = (uint32_t)t.part_slot + (uint32_t)u * nks;
+    float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < nks; p0 += kFinBatch) {
+      u32x4 pv[kFinBatch], pu[kFinBatch];
+      Spin sp = spin_start();
+      for (;;) {
+#pragma unroll
+        for (int q = 0; q < kFinBatch; ++q) {
+          const bool ok = p0 + q < nks;
+          const uint32_t base = (slot0 + (uint32_t)(p0 + q)) * 1024u;
+          pv[q] = ok ? co_load16(pbase, base + 16u * lane) : u32x4{1u, 1u, 1u, 1u};
+          pu[q] = (ok && gu) ? co_load16(pbase, base + 16u * (lane ^ 8)) : u32x4{1u, 1u, 1u, 1u};
+        }
+        uint32_t flags = 1u;
+#pragma unroll
+        for (int q = 0; q < kFinBatch; ++q)
+          flags &= pv[q].x & pv[q].y & pv[q].z & pv[q].w & pu[q].x & pu[q].y & pu[q].z & pu[q].w;
+        if (__all((flags & 1u) != 0)) break;
+        if (!poll_ok(A, c, sp)) return false;
+      }
+#pragma unroll
+      for (int q = 0; q < kFinBatch; ++q) {
+        if (p0 + q >= nks) break;
+        co_store16(pbase, (slot0 + (uint32_t)(p0 + q)) * 1024u + 16u * lane, u32x4{0u, 0u, 0u, 0u});
+        const u32x4 a = untag4(pv[q]), b = untag4(pu[q]);
+        val[0] += __uint_as_float(a.x);
+        val[1] += __uint_as_float(a.y);
+        val[2] += __uint_as_float(a.z);
+        val[3] += __uint_as_float(a.w);
+        up[0] += __uint_as_float(b.x);
+        up[1] += __uint_as_float(b.y);
+        up[2] += __uint_as_float(b.z);
+        up[3] += __uint_as_float(b.w);
+      }
+    }
+    // residuals of the O / down epilogue, polled for their step tags
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (has_resid) {
+      Spin sp = spin_start();
+      for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = (lane >> 4) + 4 * j;
+          const bool need = n < A->b && lr < M;
+          rs[j] = need ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4)) : 0.f;
+          if (need) ok = ok & tag_ok(__float_as_uint(rs[j]), (tags >> n) & 1u);
+        }
+        if (__all(ok)) break;
+        if (!poll_ok(A, c, sp)) return false;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rs[j] = untagf(rs[j]);
+    }
+    const float nw = (has_resid && lr < M) ? bf2f(nwp[lr]) : 0.f;
+    if (!gu) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) up[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gemv_epilogue(epi, c, lr, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], nw, rmsv[j]);
+  }
+  if (t.flags & kTaskSignal) {
+    // the CU's last task of the stage; only the LM head counts its tasks
+    // (for the greedy tokens)
+    const bool lm = t.stage == ST_LM;
+    if (lm) wait_mem();
+    if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    s.synced = 1;
+    if (lm && w == 0) {
+      if (lane < A->b) {
+        const unsigned long long key = c->lmkey[lane];
+        if (key) __hip_atomic_fetch_max(keys_ptr(A) + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_mem();
+      }
+      if (lane == 0) signal_counter(A, t.signal_ctr, cu);
+    }
+  }
   return true;
 }
 
@@ -2080,7 +2227,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
       const uint64_t tw0 = MK_PHASE_TRACE && ast ? now_ticks() : 0;
       if (!wait_chunk(A, c, gq, s.w_empty)) return false;
       if (MK_PHASE_TRACE && ast) trace_add(ast + 9, now_ticks() - tw0);
-      const char* slot = ring + (size_t)(gq % A->nslot) * kChunkBytes;
+      const char* slot = ring + (size_t)(gq % A->nslot) * kSlotBytes;
       const int rows = min(RPC, P.ncached - ch * RPC);
       // scores S[head][row]: lane holds heads 4 lr + i of row rb * 16 + r16
       f32x4 S[NRB];
@@ -2361,6 +2508,9 @@ __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
     } else if (t.type == TT_ATTN) {
       ok = A->hd == 128 ? attn_dispatch<128>(A, T + ti, cu, w, lane) : attn_dispatch<64>(A, T + ti, cu, w, lane);
       nch = attn_task_chunks(A, cu, t.layer, rpc);
+    } else if (t.type == TT_FIN) {
+      ok = fin_task(A, T + ti, cu, w, lane);
+      had_lm = had_lm || t.stage == ST_LM;
     } else {
       ok = embed_task(A, T + ti, cu, w, lane);
     }
@@ -2464,7 +2614,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
 }
 
 size_t lds_bytes(int nslot, int xb_bytes) {
-  return (size_t)nslot * kChunkBytes + xb_bytes + kRedBytes + kCtrlBytes;
+  return (size_t)nslot * kSlotBytes + xb_bytes + kRedBytes + kCtrlBytes;
 }
 
 static hipError_t set_lds_limit(size_t lds) {

@@ -4,10 +4,11 @@
 // grid-wide barriers follow the ForgeMegakernel milestones ("4.1 The universal
 // knowledge base and the milestones": per-SM instruction streams, dependency
 // counters, buffer pool); the one-block-per-SM task-descriptor execution model
-// follows the Cohere megakernel digest.  Each task's dependency is recorded as
-// a counter and the deadlock check runs over those counts; on the device the
-// hand-offs poll step-tagged data instead, and only the LM head's completion
-// is still counted.
+// follows the Cohere megakernel digest.  On the device the hand-offs poll
+// step-tagged data and only the LM head's completion is counted; the deadlock
+// check here models every device wait as a wait on all of its possible
+// producers (the schedule validator of the AutoMegaKernel page: deadlock
+// freedom proven before anything runs).
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -63,6 +64,8 @@ constexpr double kWindowChunks = 4.0;         // per staged window
 
 struct Tiling {
   bool owner = false;
+  bool ks = false;     // K-split: S K pieces of at most one LDS window each, dealt K-major
+  int S = 1;           // K-split: pieces
   int gs = 4;          // stream-K: sub-tiles per group
   int tmax = 4;        // row-owner: sub-tiles per task
   int nst = 1;         // sub-tiles of the stage
@@ -110,8 +113,31 @@ Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw, int b) {
   const double own_stage = stage_cost(nkb) * (double)(nkb <= wkb ? 1 : tasks_cu);
   const double own_cost = (double)tiles_cu * nkb + 0.25 * (double)tasks_cu + own_stage;
   const bool use_owner = p.gemv_mode == 1 || (p.gemv_mode == 0 && own_cost <= best_cost);
+  // K-split: when a task's K range needs more than one staging window, cut K
+  // into S pieces of at most one window each and deal (piece, sub-tile) units
+  // K-major over the CUs, so each CU stages one input slice and streams its
+  // units against it; every piece publishes its partial tile and a finish
+  // task per CU sums the pieces of its share of the sub-tiles.  Restaging a
+  // window costs a memory round trip per window and reads the whole input on
+  // every CU; the pieces cost one 1 KB partial tile per (piece, sub-tile).
+  // Worth it only when the tiling it replaces restages many windows per task
+  // (measured: with 1-block windows at batch 16, 7-10 windows per task gained
+  // 13%; at batch 8-9, 2-3 windows of 2-3 blocks each lost 4-8%).
+  const Tiling& rep = use_owner ? own : best;
+  const long long rep_kbs = rep.owner ? nkb : std::min<long long>(nkb, (rep.ncols + p.ncu - 1) / p.ncu);
+  const long long rep_windows = (rep_kbs + wkb - 1) / wkb;
+  if (p.ksplit && p.gemv_mode == 0 && nkb > wkb && rep_windows >= p.ksplit_min_windows) {
+    Tiling k = own;
+    k.owner = false;
+    k.ks = true;
+    k.S = (nkb + wkb - 1) / wkb;
+    return k;
+  }
   return use_owner ? own : best;
 }
+
+// first K block of piece s when nkb blocks are cut into S pieces
+int piece_kb(int s, int nkb, int S) { return (int)((long long)s * nkb / S); }
 
 int owner(long long u, long long units, int ncu) { return (int)(u * ncu / units); }
 
@@ -181,6 +207,17 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
     tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st), tpw, batch);
     const Tiling& T = tl[st];
     P.stage_owner[st] = T.owner ? 1 : 0;
+    if (T.ks) {
+      // one 256-float tile slot per (sub-tile, piece), in 1024-float blocks
+      group_pieces[st].assign(1, T.S);
+      grp_base[st] = grp_counters;
+      part_base[st] = part_blocks;
+      part_blocks += (T.nst * T.S + 3) / 4;
+      P.stage_ksplit[st] = T.S;
+      P.stage_kpieces[st] = T.S;
+      P.stage_rows[st] = 16 * T.tmax;
+      continue;
+    }
     if (T.owner) {
       group_pieces[st].assign(1, 1);
       grp_base[st] = grp_counters;
@@ -221,7 +258,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   std::vector<std::vector<int>> group_part(6);
   for (int si = 0; si < 5; ++si) {
     int st = gemv_stages[si];
-    if (tl[st].owner) continue;
+    if (tl[st].owner || tl[st].ks) continue;
     group_part[st].assign(tl[st].ngroups, -1);
     int nxt = part_base[st];
     for (int g = 0; g < tl[st].ngroups; ++g)
@@ -241,6 +278,54 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
     const int M = stage_rows(pc, st), K = stage_k(pc, st);
     const Tiling& T = tl[st];
     const int nst = (M + 15) / 16;
+    if (T.ks) {
+      // units (piece s, sub-tile u), s-major, dealt evenly over the CUs; a
+      // CU's run of units with one s becomes tasks of at most tmax sub-tiles
+      const long long units = (long long)T.S * nst;
+      std::fill(prev_used.begin(), prev_used.end(), 1);
+      for (int c = 0; c < ncu; ++c) {
+        const long long u0 = units * c / ncu, u1 = units * (c + 1) / ncu;
+        for (long long x = u0; x < u1;) {
+          const int sp = (int)(x / nst), ua = (int)(x % nst);
+          const int ub = (int)std::min<long long>(nst, ua + (u1 - x));
+          for (int a = ua; a < ub; a += T.tmax) {
+            const int e = std::min(ub, a + T.tmax);
+            const int kb0 = piece_kb(sp, T.nkb, T.S), kb1 = piece_kb(sp + 1, T.nkb, T.S);
+            Task t = base_task(TT_GEMV, st, layer);
+            t.row0 = 16 * a;
+            t.nsub = e - a;
+            t.k0 = kb0 * kKBlock;
+            t.k1 = std::min(K, kb1 * kKBlock);
+            t.nks = T.S;
+            t.ks = sp;
+            t.part_slot = part_base[st] * 4;
+            t.wait_ctr = wait;
+            t.flags = kTaskPublish;
+            t.nchunks = t.nsub * (kb1 - kb0);
+            cu_bytes[c] += (long long)std::min(16 * t.nsub, M - t.row0) * (t.k1 - t.k0) * 2;
+            S[c].push_back(t);
+          }
+          x += ub - ua;
+        }
+      }
+      // finish tasks: CU c sums the pieces of sub-tiles [nst c / ncu, nst (c+1) / ncu)
+      for (int c = 0; c < ncu; ++c) {
+        const int f0 = (int)((long long)nst * c / ncu), f1 = (int)((long long)nst * (c + 1) / ncu);
+        if (f1 <= f0) continue;
+        Task t = base_task(TT_FIN, st, layer);
+        t.row0 = 16 * f0;
+        t.nsub = f1 - f0;
+        t.k0 = 0;
+        t.k1 = K;
+        t.nks = T.S;
+        t.part_slot = part_base[st] * 4;
+        t.wait_ctr = wait;
+        t.signal_ctr = signal;
+        t.flags = kTaskSignal;
+        S[c].push_back(t);
+      }
+      return;
+    }
     if (T.owner) {
       std::vector<int> cus;
       int nprev = 0;
@@ -346,7 +431,6 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
 
   // Flatten, count expected signals per counter shard.
   std::vector<int> expect((size_t)P.n_counters * kShards, 0);
-  std::vector<int> total_signals(P.n_counters, 0);
   int n_tasks = 0, max_tasks = 0;
   for (int c = 0; c < ncu; ++c) {
     n_tasks += (int)S[c].size();
@@ -354,7 +438,6 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
     for (const Task& t : S[c]) {
       if (t.signal_ctr >= 0 && (t.flags & kTaskSignal)) {
         expect[(size_t)t.signal_ctr * kShards + (c % kShards)] += 1;
-        total_signals[t.signal_ctr] += 1;
       }
     }
   }
@@ -363,7 +446,8 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   // (1) every (row, K element) of every GEMV stage is covered exactly once:
   //     per sub-tile, the K ranges of the tasks covering it tile [0, K) in
   //     piece order; split groups carry consistent piece indices; chunk
-  //     counts match the task shapes.
+  //     counts match the task shapes; a K-split stage's sub-tiles are each
+  //     finished by exactly one finish task.
   for (int l = 0; l <= pc.L; ++l) {
     for (int si = 0; si < 5; ++si) {
       int st = gemv_stages[si];
@@ -371,17 +455,32 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
       const Tiling& T = tl[st];
       const int M = stage_rows(pc, st), K = stage_k(pc, st);
       const int nst = (M + 15) / 16;
-      std::vector<int> next_k(nst, 0), pieces(nst, 0);
+      std::vector<int> next_k(nst, 0), pieces(nst, 0), fins(nst, 0);
       long long covered = 0;
       for (int cu = 0; cu < ncu; ++cu)
         for (const Task& t : S[cu]) {
-          if (t.type != TT_GEMV || t.stage != st || t.layer != l) continue;
+          if (t.stage != st || t.layer != l) continue;
+          if (t.type == TT_FIN) {
+            if (!T.ks || t.nks != T.S || t.part_slot != part_base[st] * 4 || t.nsub < 1 || t.row0 % 16 ||
+                t.row0 / 16 + t.nsub > nst || t.nchunks != 0)
+              return MK_ERR_PLAN;
+            for (int u = t.row0 / 16; u < t.row0 / 16 + t.nsub; ++u) fins[u] += 1;
+            continue;
+          }
+          if (t.type != TT_GEMV) continue;
           if (t.row0 % 16 || t.nsub < 1 || t.nsub > 4 * tpw || t.row0 / 16 + t.nsub > nst) return MK_ERR_PLAN;
           if (t.k0 % kKBlock || t.k1 <= t.k0 || t.k1 > K) return MK_ERR_PLAN;
           if (t.nchunks != t.nsub * ((t.k1 - t.k0 + kKBlock - 1) / kKBlock)) return MK_ERR_PLAN;
           if (T.owner && (t.nks != 1 || t.k0 != 0 || t.k1 != K)) return MK_ERR_PLAN;
-          if (!T.owner && (t.nsub > T.gs || t.row0 != t.group * 16 * T.gs || t.nks != group_pieces[st][t.group]))
+          if (T.ks) {
+            const int wkb = std::max(1, ((pc.xb_bytes / (4 * batch)) - 8) / kKBlock);
+            if (!(t.flags & kTaskPublish) || t.nks != T.S || t.part_slot != part_base[st] * 4 ||
+                (t.k1 - t.k0 + kKBlock - 1) / kKBlock > wkb || t.k0 != piece_kb(t.ks, T.nkb, T.S) * kKBlock)
+              return MK_ERR_PLAN;
+          } else if (!T.owner &&
+                     (t.nsub > T.gs || t.row0 != t.group * 16 * T.gs || t.nks != group_pieces[st][t.group])) {
             return MK_ERR_PLAN;
+          }
           for (int u = t.row0 / 16; u < t.row0 / 16 + t.nsub; ++u) {
             if (t.k0 != next_k[u] || t.ks != pieces[u]) return MK_ERR_PLAN;
             next_k[u] = t.k1;
@@ -391,32 +490,87 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
         }
       for (int u = 0; u < nst; ++u) {
         if (next_k[u] != K) return MK_ERR_PLAN;
-        if (!T.owner && pieces[u] != group_pieces[st][u / T.gs]) return MK_ERR_PLAN;
+        if (T.ks && (pieces[u] != T.S || fins[u] != 1)) return MK_ERR_PLAN;
+        if (!T.owner && !T.ks && pieces[u] != group_pieces[st][u / T.gs]) return MK_ERR_PLAN;
       }
       if (covered != (long long)M * K) return MK_ERR_PLAN;
     }
   }
-  // (2) deadlock freedom: execute the in-order streams abstractly; a task may
-  //     run once every signal of the counter it waits on has been given.
+  // (2) deadlock freedom.  The device has three kinds of wait, each modelled
+  //     here as a wait on ALL the tasks that could produce what it polls (a
+  //     superset of its real producers, so a schedule that completes here
+  //     cannot deadlock on the device):
+  //       * a stage's inputs (step-tagged words of the previous stage's
+  //         output): every task of that stage;
+  //       * a split group's piece 0 (after its own piece), a K-split finish
+  //         task: every piece of the stage in that layer;
+  //       * attention's segment finisher (after the CU's own pieces): every
+  //         attention piece of the layer (the partition is cut on the device).
+  //     Each task is one or two phases (wait, signal); the in-order streams
+  //     run abstractly until nothing can move.
   {
-    std::vector<int> given(P.n_counters, 0);
-    std::vector<size_t> pc_(ncu, 0);
+    const int kStages = 7;  // QKV ATTN O GU DOWN LM EMBED
+    auto out_ctr = [&](int st, int l) { return 2 * (l * kStages + st); };
+    auto piece_ctr = [&](int st, int l) { return 2 * (l * kStages + st) + 1; };
+    auto prev_out = [&](int st, int l) {
+      switch (st) {
+        case ST_QKV: return l == 0 ? out_ctr(ST_EMBED, 0) : out_ctr(ST_DOWN, l - 1);
+        case ST_ATTN: return out_ctr(ST_QKV, l);
+        case ST_O: return out_ctr(ST_ATTN, l);
+        case ST_GU: return out_ctr(ST_O, l);
+        case ST_DOWN: return out_ctr(ST_GU, l);
+        case ST_LM: return out_ctr(ST_DOWN, pc.L - 1);
+      }
+      return -1;
+    };
+    struct Ph {
+      int wait, signal;
+    };
+    const int nctr = 2 * (pc.L + 1) * kStages;
+    std::vector<std::vector<Ph>> prog(ncu);
+    std::vector<int> total(nctr, 0), given(nctr, 0);
+    for (int c = 0; c < ncu; ++c)
+      for (const Task& t : S[c]) {
+        const int l = t.layer;
+        if (t.type == TT_EMBED) {
+          prog[c].push_back({-1, out_ctr(ST_EMBED, 0)});
+        } else if (t.type == TT_ATTN) {
+          prog[c].push_back({prev_out(ST_ATTN, l), piece_ctr(ST_ATTN, l)});
+          prog[c].push_back({piece_ctr(ST_ATTN, l), out_ctr(ST_ATTN, l)});
+        } else if (t.type == TT_FIN) {
+          prog[c].push_back({piece_ctr(t.stage, l), out_ctr(t.stage, l)});
+        } else if (t.flags & kTaskPublish) {
+          prog[c].push_back({prev_out(t.stage, l), piece_ctr(t.stage, l)});
+        } else if (t.nks > 1) {
+          prog[c].push_back({prev_out(t.stage, l), piece_ctr(t.stage, l)});
+          if (t.ks == 0) prog[c].push_back({piece_ctr(t.stage, l), out_ctr(t.stage, l)});
+        } else {
+          prog[c].push_back({prev_out(t.stage, l), out_ctr(t.stage, l)});
+        }
+      }
+    size_t nph = 0;
+    for (int c = 0; c < ncu; ++c)
+      for (const Ph& ph : prog[c]) {
+        total[ph.signal] += 1;
+        nph += 1;
+      }
+    std::vector<size_t> pcx(ncu, 0);
     size_t done = 0;
     bool progress = true;
     while (progress) {
       progress = false;
       for (int c = 0; c < ncu; ++c) {
-        while (pc_[c] < S[c].size()) {
-          const Task& t = S[c][pc_[c]];
-          if (t.wait_ctr >= 0 && given[t.wait_ctr] < total_signals[t.wait_ctr]) break;
-          if (t.signal_ctr >= 0 && (t.flags & kTaskSignal)) given[t.signal_ctr] += 1;
-          pc_[c] += 1;
+        while (pcx[c] < prog[c].size()) {
+          const Ph& ph = prog[c][pcx[c]];
+          if (ph.wait >= 0 && (total[ph.wait] == 0 || given[ph.wait] < total[ph.wait])) break;
+          given[ph.signal] += 1;
+          pcx[c] += 1;
           done += 1;
           progress = true;
         }
       }
     }
-    if (done != (size_t)n_tasks) return MK_ERR_PLAN;
+    if (done != nph) return MK_ERR_PLAN;
   }
 
   // ---- stats & output ----------------------------------------------------

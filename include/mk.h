@@ -252,6 +252,8 @@ typedef struct {
   int32_t stage_shared_prev[6];
   int32_t attn_slot_cap;        /* attention slot cap of that layer (0: none) */
   int32_t attn_slots_valid;     /* 1: every layer's attention slots are a permutation of the CUs */
+  int32_t stage_kpieces[6];     /* K-split stages: K pieces (each piece publishes partial tiles that
+                                   per-CU finish tasks sum); 0 for other tilings */
 } mk_plan_stats;
 
 int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats* out);
