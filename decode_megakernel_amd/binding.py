@@ -17,7 +17,7 @@ STATUS_BAD_POSITION = 2
 STATUS_BAD_SEQLEN = 4
 STATUS_TIMEOUT = 8
 ERRORS = {-1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_OOM", -4: "MK_ERR_HIP",
-          -5: "MK_ERR_PLAN"}
+          -5: "MK_ERR_PLAN", -6: "MK_ERR_TOO_LARGE"}
 
 
 class MKError(RuntimeError):
@@ -59,7 +59,7 @@ class PlanStats(ctypes.Structure):
                 ("attn_slots_valid", ctypes.c_int32), ("stage_kpieces", ctypes.c_int32 * 6)]
 
 
-EXPORTS = ["mk_create", "mk_decode_step", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
+EXPORTS = ["mk_create", "mk_decode_step", "mk_decode_step_static", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
            "mk_reset", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
 STAT_WORDS = 80  # per-CU trace totals, see mk_copy_trace
@@ -77,6 +77,7 @@ def lib():
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     L.mk_create.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(WeightPtrs), ctypes.POINTER(vp)]
     L.mk_decode_step.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp]
+    L.mk_decode_step_static.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp]
     L.mk_copy_hidden.argtypes = [vp, i32, vp, vp]
     L.mk_copy_state.argtypes = [vp, i32, i32, vp, vp]
     L.mk_copy_trace.argtypes = [vp, vp, ctypes.c_int64, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
@@ -168,18 +169,19 @@ class DecodeEngine:
         self.max_batch = max_batch
 
     def step(self, tokens, positions, seq_lens, k_cache, v_cache, logits, next_tokens=None, stream=None,
-             batch=None):
+             batch=None, static=False):
         """Enqueue one decode step; all tensors are CUDA tensors the caller owns.
 
         k_cache, v_cache: bf16 [L][batch_cap][n_kv][seq_cap][hd]; tokens, positions,
-        seq_lens: int32 [>= batch]; logits: float32 [>= batch, vocab]."""
+        seq_lens: int32 [>= batch]; logits: float32 [>= batch, vocab].  static=True
+        calls the allocation-free entry point (scratch in the library's static array)."""
         b = int(tokens.numel()) if batch is None else int(batch)
         kv = KVCache(k_cache.data_ptr(), v_cache.data_ptr(), int(k_cache.shape[1]), int(k_cache.shape[3]))
-        rc = lib().mk_decode_step(self.handle, b, tokens.data_ptr(), positions.data_ptr(), seq_lens.data_ptr(),
-                                  ctypes.byref(kv), logits.data_ptr(),
-                                  None if next_tokens is None else next_tokens.data_ptr(),
-                                  _stream_handle(stream))
-        _check(rc, "mk_decode_step")
+        fn = lib().mk_decode_step_static if static else lib().mk_decode_step
+        rc = fn(self.handle, b, tokens.data_ptr(), positions.data_ptr(), seq_lens.data_ptr(),
+                ctypes.byref(kv), logits.data_ptr(), None if next_tokens is None else next_tokens.data_ptr(),
+                _stream_handle(stream))
+        _check(rc, "mk_decode_step_static" if static else "mk_decode_step")
 
     def copy_hidden(self, batch: int, out, stream=None):
         _check(lib().mk_copy_hidden(self.handle, int(batch), out.data_ptr(), _stream_handle(stream)),

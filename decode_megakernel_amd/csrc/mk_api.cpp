@@ -16,6 +16,8 @@
 namespace mk {
 hipError_t launch_step(const DevArgs& A, hipStream_t stream, bool coop);
 hipError_t step_occupancy(size_t lds, int* blocks_per_cu);
+hipError_t static_scratch_base(void** out);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_untag_copy(void* dst, size_t dpitch, const void* src, size_t spitch, size_t row_bytes, size_t rows,
                              hipStream_t stream);
 size_t lds_bytes(int nslot, int xb_bytes);
@@ -72,6 +74,12 @@ struct mk_handle {
   size_t part_bytes = 0;
   int coop = 1;                     // cooperative launches (co-residency guaranteed by the runtime)
   float* dump = nullptr;            // caller's mid-state dump buffer (mk_set_midstate_dump), NULL = off
+  // workspace offsets: the allocation-free step lays the same buffers out in
+  // the static scratch array (activations and partials from offset 0, the
+  // counter banks at o_banks, the split-K slots at o_part)
+  size_t o_hres = 0, o_hmid = 0, o_xattn = 0, o_xmlp = 0, o_ssattn = 0, o_ssmlp = 0, o_qkv = 0, o_aout = 0,
+         o_act = 0, o_apart = 0, o_banks = 0, o_part = 0, static_bytes = 0;
+  void* sbase = nullptr;            // this device's static scratch array (looked up at mk_create)
   uint64_t step = 0;
   uint64_t* trace = nullptr;   // MK_TRACE=<tasks per CU>: per-task timestamps + per-CU wait totals
   int trace_cap = 0;
@@ -88,6 +96,7 @@ const char* mk_error_string(int code) {
     case MK_ERR_OOM: return "device out of memory";
     case MK_ERR_HIP: return "HIP runtime error";
     case MK_ERR_PLAN: return "schedule validation failed";
+    case MK_ERR_TOO_LARGE: return "the step's scratch exceeds the static scratch array (64 MiB per GPU)";
   }
   return "unknown error";
 }
@@ -292,6 +301,18 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   size_t o_zero = take(1024);
   h->ws_bytes = off;
   h->tagged_bytes = o_banks;  // hres .. apart: words that carry step tags / validity flags
+  h->o_hres = o_hres;
+  h->o_hmid = o_hmid;
+  h->o_xattn = o_xattn;
+  h->o_xmlp = o_xmlp;
+  h->o_ssattn = o_ssattn;
+  h->o_ssmlp = o_ssmlp;
+  h->o_qkv = o_qkv;
+  h->o_aout = o_aout;
+  h->o_act = o_act;
+  h->o_apart = o_apart;
+  h->o_banks = o_banks;
+  h->o_part = o_status;  // the banks end here
   if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
     delete h;
     return MK_ERR_OOM;
@@ -408,6 +429,12 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
     mk_destroy(h);
     return MK_ERR_HIP;
   }
+  // set-up of the allocation-free step: this device's static scratch array
+  h->static_bytes = h->o_part + h->part_bytes;
+  if (static_scratch_base(&h->sbase) != hipSuccess) {
+    mk_destroy(h);
+    return MK_ERR_HIP;
+  }
   int coop_ok = 0;
   if (hipDeviceGetAttribute(&coop_ok, hipDeviceAttributeCooperativeLaunch, h->device) != hipSuccess) coop_ok = 0;
   h->coop = coop_ok && env_int("MK_COOP", 1) != 0;
@@ -457,9 +484,11 @@ static size_t part_bytes_of(const mk_handle* h, const GraphDev& g) {
   return sizeof(float) * 1024 * (size_t)(h->cfg.n_layers + 1) * std::max(1, g.plan.part_blocks);
 }
 
-int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
-                   const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out, int32_t* next_tokens_out,
-                   void* stream) {
+// Checks and kernel arguments shared by both step entry points; the
+// workspace pointers are the handle's own.
+static int step_args(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                     const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out, int32_t* next_tokens_out,
+                     DevArgs& A, GraphDev** gout) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (batch < 0 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
   if (batch == 0) return MK_OK;
@@ -469,8 +498,8 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   auto git = h->graphs.find(batch);
   if (git == h->graphs.end()) return MK_ERR_INVALID_ARG;  // every batch 1..max_batch is built by mk_create
   GraphDev* g = &git->second;
+  *gout = g;
   const mk_model_cfg& c = h->cfg;
-  DevArgs A;
   memset(&A, 0, sizeof(A));
   A.L = c.n_layers;
   A.d = c.hidden;
@@ -536,9 +565,54 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
   A.trace_cap = h->trace_cap;
   A.attn_pad = h->attn_pad;
   A.dump = h->dump;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                   const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out, int32_t* next_tokens_out,
+                   void* stream) {
+  DevArgs A;
+  GraphDev* g = nullptr;
+  int rc = step_args(h, batch, tokens, positions, seq_lens, kv, logits_out, next_tokens_out, A, &g);
+  if (rc || batch == 0) return rc;
   if (launch_step(A, (hipStream_t)stream, h->coop != 0) != hipSuccess) return MK_ERR_HIP;
   h->rowtag = A.rowtag;
   h->step += 1;
+  return MK_OK;
+}
+
+int mk_decode_step_static(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                          const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
+                          int32_t* next_tokens_out, void* stream) {
+  DevArgs A;
+  GraphDev* g = nullptr;
+  int rc = step_args(h, batch, tokens, positions, seq_lens, kv, logits_out, next_tokens_out, A, &g);
+  if (rc || batch == 0) return rc;
+  if (h->static_bytes > kStaticScratchBytes) return MK_ERR_TOO_LARGE;
+  if (!h->sbase) return MK_ERR_HIP;
+  // the same buffers at the same offsets inside the static array, cleared on
+  // the caller's stream first (it keeps the previous call's contents): every
+  // activation word then carries tag 0, so this step's sequences use tag 1,
+  // and every partial slot and counter starts at zero
+  char* base = (char*)h->sbase;
+  A.hres = (float*)(base + h->o_hres);
+  A.hmid = (float*)(base + h->o_hmid);
+  A.xattn = (float*)(base + h->o_xattn);
+  A.xmlp = (float*)(base + h->o_xmlp);
+  A.ssattn = (float*)(base + h->o_ssattn);
+  A.ssmlp = (float*)(base + h->o_ssmlp);
+  A.qkv = (float*)(base + h->o_qkv);
+  A.attn_out = (float*)(base + h->o_aout);
+  A.act = (float*)(base + h->o_act);
+  A.apart = (float*)(base + h->o_apart);
+  A.banks = (uint32_t*)(base + h->o_banks);
+  A.part = (float*)(base + h->o_part);
+  A.rowtag = (1u << batch) - 1u;
+  A.bank = 0;
+  A.trace = nullptr;
+  A.trace_cap = 0;
+  if (launch_zero(base, h->static_bytes, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  if (launch_step(A, (hipStream_t)stream, h->coop != 0) != hipSuccess) return MK_ERR_HIP;
   return MK_OK;
 }
 

@@ -47,7 +47,10 @@ constexpr int attn_lds_floats(int hd, int gm) {
 }
 constexpr int kAttnStateBytes =
     4 * (attn_lds_floats(64, 8) > attn_lds_floats(128, 4) ? attn_lds_floats(64, 8) : attn_lds_floats(128, 4));
-constexpr int kStatWords = 80;               // trace: per-CU phase totals (uint64 words)
+constexpr int kStatWords = 80;
+// Scratch of the allocation-free step (mk_decode_step_static): one file-scope
+// device array per GPU, held until the process ends.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;               // trace: per-CU phase totals (uint64 words)
 #ifndef MK_PHASE_TRACE
 #define MK_PHASE_TRACE 0
 #endif

@@ -21,6 +21,7 @@
 
 #include "mk_internal.h"
 
+#include <mutex>
 #include <utility>
 
 // Per-phase timers of the in-kernel trace (per-CU stats words 32..61).  They
@@ -2648,6 +2649,45 @@ hipError_t launch_step(const DevArgs& A, hipStream_t stream, bool coop) {
                                       stream);
   }
   hipLaunchKernelGGL(mk_step_kernel, dim3(A.ncu), dim3(kThreads), lds, stream, A);
+  return hipGetLastError();
+}
+
+// ---- scratch of the allocation-free step: a file-scope device array.  Host
+// code never uses the array's name as an address: its device address is
+// looked up once per device (with that device current) and kept.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_base(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* base[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    base[dev] = p;
+  }
+  *out = base[dev];
+  return hipSuccess;
+}
+
+// Zero `bytes` (a multiple of 16) at p: a kernel rather than a memset node, so
+// a caller may capture the call into a graph.
+__global__ void mk_zero_kernel(u32x4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+  hipLaunchKernelGGL(mk_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)p, n);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ extern "C" {
 #define MK_ERR_OOM (-3)           /* device allocation failed */
 #define MK_ERR_HIP (-4)           /* a HIP runtime call failed */
 #define MK_ERR_PLAN (-5)          /* the schedule failed validation (never expected) */
+#define MK_ERR_TOO_LARGE (-6)     /* mk_decode_step_static: the handle's scratch exceeds the static array */
 
 /* Device status bits (mk_get_status).  Each bad value is clamped on the
  * device so nothing is read or written out of bounds. */
@@ -142,6 +143,24 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
 int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
                    const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
                    int32_t* next_tokens_out, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step as mk_decode_step -- same arguments, kernel, schedules and results --
+ * with all the kernel's scratch (per-layer activations, split-K and attention
+ * partials, counter banks) in one file-scope device array of the library, 64
+ * MiB per GPU, held until the process ends, instead of the handle's
+ * workspace.  It calls no allocating routine: it enqueues a fill kernel that
+ * clears the used part of the array, then the step launch.  Returns
+ * MK_ERR_TOO_LARGE when the handle's scratch (set by the model, max_batch and
+ * the schedules) does not fit the array.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other handles)
+ * race, and mk_copy_hidden / mk_copy_state / mk_copy_trace do not see a
+ * static step's mid-states (mk_set_midstate_dump does).  Status bits go to
+ * the handle, as for mk_decode_step. */
+int mk_decode_step_static(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                          const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
+                          int32_t* next_tokens_out, void* stream);
 
 /* Copy the residual stream of the last step, enqueued on `stream` (the
  * per-layer hidden states the mid-state oracle checks: the ForgeMegakernel
