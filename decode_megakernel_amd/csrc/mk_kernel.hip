@@ -689,15 +689,19 @@ __device__ __forceinline__ void dma_gemv_chunk(DArgs A, const RowBase& rb, int k
   }
 }
 
-// One attention chunk: RPC cached K rows, then the same V rows.
+// One attention chunk: RPC cached K rows, then the same V rows.  With `rot`
+// (one query head per KV head: the VALU attention tiles) row r's 16-byte
+// groups are stored rotated by r & 7, so LDS position p of row r holds group
+// (p + (r & 7)) mod (groups per row).
 template <int HD>
 __device__ __forceinline__ void dma_attn_chunk(DArgs A, const uint16_t* kbase, const uint16_t* vbase, int rows, int lane,
-                                               char* dst) {
+                                               char* dst, bool rot) {
   constexpr int LPR = HD / 8, RP = 64 / LPR;
-  const int e = (lane % LPR) * 8;
+  const int pos = lane % LPR;
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
     const int rl = (j & 7) * RP + lane / LPR;
+    const int e = (rot ? ((pos + (rl & 7)) & (LPR - 1)) : pos) * 8;
     const uint16_t* src = (j < 8 ? kbase : vbase) + (size_t)rl * HD + e;
     dma16(rl < rows ? (const void*)src : (const void*)A->zero, dst + j * 1024);
   }
@@ -811,8 +815,8 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
           const size_t row0 = (head + P.j0 + (size_t)ch * rpc) * A->hd;
           const int rows = min(rpc, P.ncached - ch * rpc);
           char* dst = ring + (size_t)R.slot * kSlotBytes;
-          if (A->hd == 128) dma_attn_chunk<128>(A, A->kc + row0, A->vc + row0, rows, lane, dst);
-          else dma_attn_chunk<64>(A, A->kc + row0, A->vc + row0, rows, lane, dst);
+          if (A->hd == 128) dma_attn_chunk<128>(A, A->kc + row0, A->vc + row0, rows, lane, dst, A->G == 1);
+          else dma_attn_chunk<64>(A, A->kc + row0, A->vc + row0, rows, lane, dst, A->G == 1);
           ring_issued(A, c, R, lane);
         }
         pbase += P.nch;
@@ -950,6 +954,54 @@ __device__ __forceinline__ bool poll_ss(DArgs A, Ctrl* c, const float* ss, int n
     if (__all(ok)) return true;
     if (!poll_ok(A, c, sp)) return false;
   }
+}
+
+// RMS scales of sequences w, w + 4, ... (< b) into the control block: all
+// their per-16-row sums of squares are loaded in one batch and polled until
+// each carries its sequence's step tag (one memory round trip for up to four
+// sequences per wave).  `first` holds a first attempt for sequence w when
+// `loaded`.
+__device__ __forceinline__ bool rms_scales(DArgs A, Ctrl* c, const float* ss, int w, int lane, uint32_t tags,
+                                           const uint32_t (&first)[kSsLoads], bool loaded) {
+  constexpr int kSeq = kMaxBatch / kComputeWaves;
+  const int nt = A->d / 16;
+  uint32_t u[kSeq][kSsLoads];
+  Spin sp = spin_start();
+  for (;;) {
+#pragma unroll
+    for (int j = 0; j < kSeq; ++j) {
+      const int n = w + kComputeWaves * j;
+      const uint32_t tg = (tags >> n) & 1u;
+#pragma unroll
+      for (int k = 0; k < kSsLoads; ++k) {
+        const int i = lane + 64 * k;
+        if (j == 0 && loaded) u[j][k] = first[k];
+        else u[j][k] = (n < A->b && i < nt) ? co_load4(ss, (uint32_t)(((size_t)i * A->bcap + n) * 4)) : tg;
+      }
+    }
+    loaded = false;
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < kSeq; ++j) {
+      const uint32_t tg = (tags >> (w + kComputeWaves * j)) & 1u;
+#pragma unroll
+      for (int k = 0; k < kSsLoads; ++k) ok = ok & tag_ok(u[j][k], tg);
+    }
+    if (__all(ok)) break;
+    if (!poll_ok(A, c, sp)) return false;
+  }
+#pragma unroll
+  for (int j = 0; j < kSeq; ++j) {
+    const int n = w + kComputeWaves * j;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSsLoads; ++k) acc += lane + 64 * k < nt ? __uint_as_float(untag(u[j][k])) : 0.f;
+    acc = group_sum<16>(acc);
+    acc = swap16_sum(acc, acc);
+    acc = swap32_sum(acc, acc);
+    if (lane == 0 && n < A->b) c->rms[n] = 1.0f / sqrtf(acc / (float)A->d + A->eps);
+  }
+  return true;
 }
 
 // ---- stage the GEMV input slice x[n][kk0:kk1) (bf16, n < b) into LDS with
@@ -1696,24 +1748,14 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
   const int M = stage_M(A, t.stage);
   const int row = lane & 15;
   const uint32_t tags = A->rowtag;
-  // every compute wave is done with the previous task's LDS before the RMS
-  // scales are rewritten
-  if (!s.synced && !cbar(A, c, s.gen, lane, &s.w_bar)) return false;
-  s.synced = 0;
+  // RMS scales of a normalised stage (one batch of loads per wave), written
+  // once every compute wave is done with the previous task's scales
   const float* ss = stage_ss(A, t.stage, t.layer);
   if (ss && !(s.r_stage == t.stage && s.r_layer == t.layer)) {
-    const int nt = A->d / 16;
-    for (int n = w; n < A->b; n += kComputeWaves) {
-      uint32_t ssu[kSsLoads];
-      if (!poll_ss(A, c, ss, n, nt, (tags >> n) & 1u, lane, ssu, false)) return false;
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < kSsLoads; ++k) acc += lane + 64 * k < nt ? __uint_as_float(untag(ssu[k])) : 0.f;
-      acc = group_sum<16>(acc);
-      acc = swap16_sum(acc, acc);
-      acc = swap32_sum(acc, acc);
-      if (lane == 0) c->rms[n] = 1.0f / sqrtf(acc / (float)A->d + A->eps);
-    }
+    if (!s.synced && !cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+    s.synced = 0;
+    uint32_t none[kSsLoads] = {};
+    if (!rms_scales(A, c, ss, w, lane, tags, none, false)) return false;
     s.r_stage = t.stage;
     s.r_layer = t.layer;
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
@@ -1738,9 +1780,10 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
     const int u = t.row0 / 16 + k;
     const int lr = 16 * u + row;
     // the piece values of this lane (rows lane & 15) and, for gate/up, of
-    // lane ^ 8 (a gate row's up row is 8 rows further in the tile)
+    // lane ^ 8 (a gate row's up row is 8 rows further in the tile); the
+    // residuals of O / down in flight with the first batch
     const uint32_t slot0 = (uint32_t)t.part_slot + (uint32_t)u * nks;
-    float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+    float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f}, rs[4] = {0.f, 0.f, 0.f, 0.f};
     for (int p0 = 0; p0 < nks; p0 += kFinBatch) {
       u32x4 pv[kFinBatch], pu[kFinBatch];
       Spin sp = spin_start();
@@ -1752,11 +1795,21 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
           pv[q] = ok ? co_load16(pbase, base + 16u * lane) : u32x4{1u, 1u, 1u, 1u};
           pu[q] = (ok && gu) ? co_load16(pbase, base + 16u * (lane ^ 8)) : u32x4{1u, 1u, 1u, 1u};
         }
+        bool rok = true;
+        if (has_resid && p0 == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = (lane >> 4) + 4 * j;
+            const bool need = n < A->b && lr < M;
+            rs[j] = need ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4)) : 0.f;
+            if (need) rok = rok & tag_ok(__float_as_uint(rs[j]), (tags >> n) & 1u);
+          }
+        }
         uint32_t flags = 1u;
 #pragma unroll
         for (int q = 0; q < kFinBatch; ++q)
           flags &= pv[q].x & pv[q].y & pv[q].z & pv[q].w & pu[q].x & pu[q].y & pu[q].z & pu[q].w;
-        if (__all((flags & 1u) != 0)) break;
+        if (__all(rok && (flags & 1u) != 0)) break;
         if (!poll_ok(A, c, sp)) return false;
       }
 #pragma unroll
@@ -1774,25 +1827,8 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
         up[3] += __uint_as_float(b.w);
       }
     }
-    // residuals of the O / down epilogue, polled for their step tags
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    if (has_resid) {
-      Spin sp = spin_start();
-      for (;;) {
-        bool ok = true;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = (lane >> 4) + 4 * j;
-          const bool need = n < A->b && lr < M;
-          rs[j] = need ? co_loadf(hin, (uint32_t)(((size_t)n * A->d + lr) * 4)) : 0.f;
-          if (need) ok = ok & tag_ok(__float_as_uint(rs[j]), (tags >> n) & 1u);
-        }
-        if (__all(ok)) break;
-        if (!poll_ok(A, c, sp)) return false;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rs[j] = untagf(rs[j]);
-    }
+    for (int j = 0; j < 4; ++j) rs[j] = untagf(rs[j]);
     const float nw = (has_resid && lr < M) ? bf2f(nwp[lr]) : 0.f;
     if (!gu) {
 #pragma unroll
@@ -1802,13 +1838,12 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
     for (int j = 0; j < 4; ++j) gemv_epilogue(epi, c, lr, row, (lane >> 4) + 4 * j, val[j], up[j], rs[j], nw, rmsv[j]);
   }
   if (t.flags & kTaskSignal) {
-    // the CU's last task of the stage; only the LM head counts its tasks
-    // (for the greedy tokens)
-    const bool lm = t.stage == ST_LM;
-    if (lm) wait_mem();
+    // the LM head's last finish task on this CU: fold the CU's argmax keys
+    // into the global ones and count the task (for the greedy tokens)
+    wait_mem();
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     s.synced = 1;
-    if (lm && w == 0) {
+    if (w == 0) {
       if (lane < A->b) {
         const unsigned long long key = c->lmkey[lane];
         if (key) __hip_atomic_fetch_max(keys_ptr(A) + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1943,6 +1978,10 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   float* pb = knv + kAttnBatch * 2 * HD + w * RPC * GM;  // P^T: 2 planes x GM heads x RPC bf16
   const float* qkv_l = A->qkv + (size_t)l * A->bcap * A->nqkv;
   const uint32_t tags = A->rowtag;
+  // the staging buffer is rewritten below (queries, new rows, wave states):
+  // every compute wave must be done with the previous task's use of it
+  if (!s.synced && !cbar(A, c, s.gen, lane, &s.w_bar)) return false;
+  s.synced = 0;
   // trace: attention phase totals of compute wave 0 (per-CU stats words 32..41)
   uint64_t* ast = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0) ? MK_PSTAT(c, 0) : nullptr;
   uint64_t tlast = ast ? now_ticks() : 0;
@@ -2190,6 +2229,154 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     next_piece(c, A->b, A->nkv, RPC, pad, bpos, hi, P);
     if (ast) trace_add(ast + 7, 1);
     const float* qk = qs + (size_t)bk * GM * HD;  // this piece's scaled queries
+    float* sb = stb + (pidx & 1) * stride_st + w * GM * SW;  // this wave's state of the piece
+    if constexpr (GM == 1) {
+      // One query head per KV head: an MFMA tile would use one of its 16 rows,
+      // so the VALU does it.  Lane l takes K/V row l / LPV of every chunk and
+      // the 64 dims (l % LPV) * 64 .. + 63; the loader stored row r's 16-byte
+      // groups rotated by r & 7 (attn_rot), so the lanes of one LDS access
+      // fall in different banks while each lane keeps fixed dims.  Scores:
+      // v_dot2 of the bf16 K row with q as bf16 hi + lo; softmax state
+      // wave-uniform; P.V accumulates each lane's row in fp32 and the rows are
+      // summed across lanes once per piece.
+      constexpr int LPV = HD / 64;  // lanes per row
+      constexpr int GPR = HD / 8;   // 16-byte groups per row
+      static_assert(64 / LPV == RPC, "one row per lane group per chunk");
+      const int vrow = lane / LPV, hh = lane % LPV, rot = vrow & 7;
+      uint32_t goff[8];  // byte offset of this lane's group i inside its row
+#pragma unroll
+      for (int i = 0; i < 8; ++i) goff[i] = (uint32_t)((((hh * 8 + i) - rot) & (GPR - 1)) * 16);
+      u32x4 qh[8], ql[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const char* src = (const char*)(qk + hh * 64 + i * 8);
+        split8(lds_ld16(src), lds_ld16(src + 16), qh[i], ql[i]);
+      }
+      float o[64];
+#pragma unroll
+      for (int d = 0; d < 64; ++d) o[d] = 0.f;
+      float m1 = -INFINITY, l1 = 0.f;
+      mark(0);
+      for (int ch = 0; ch < P.nch; ++ch) {
+        const int gq = qc + ch;
+        if ((gq & (kComputeWaves - 1)) != w) continue;
+        const uint64_t tw0 = MK_PHASE_TRACE && ast ? now_ticks() : 0;
+        if (!wait_chunk(A, c, gq, s.w_empty)) return false;
+        if (MK_PHASE_TRACE && ast) trace_add(ast + 9, now_ticks() - tw0);
+        const char* slot = ring + (size_t)(gq % A->nslot) * kSlotBytes;
+        const int rows = min(RPC, P.ncached - ch * RPC);
+        const char* kr = slot + (size_t)vrow * HD * 2;
+        float sc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4 kv = lds_ld16(kr + goff[i]);
+          sc = dot8_bf16(kv, qh[i], dot8_bf16(kv, ql[i], sc));
+        }
+        if constexpr (LPV == 2) sc += dpp_f<kDppXor1>(sc);
+        sc = vrow < rows ? sc : -INFINITY;
+        float mx = group_max<16>(sc);
+        mx = swap16_max(mx);
+        mx = swap32_max(mx);
+        const float mnew = fmaxf(m1, mx);  // finite: every chunk has a row
+        const float fa = fast_exp2(m1 - mnew);
+        const float pv = fast_exp2(sc - mnew);  // 0 for rows past the chunk
+        float ps = hh == 0 ? pv : 0.f;
+        ps = group_sum<16>(ps);
+        ps = swap16_sum(ps, ps);
+        ps = swap32_sum(ps, ps);
+        l1 = l1 * fa + ps;
+        if (fa != 1.f) {
+#pragma unroll
+          for (int d = 0; d < 64; ++d) o[d] *= fa;
+        }
+        m1 = mnew;
+        const char* vr = slot + 8192 + (size_t)vrow * HD * 2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float vf[8];
+          unpack8(lds_ld16(vr + goff[i]), vf);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o[i * 8 + u] += pv * vf[u];
+        }
+        free_chunk(A, c, gq, lane);
+      }
+      // the new row (K, V rounded to bf16, already in the cache), absorbed by
+      // wave 0: every lane forms the score from its own dims, row 0's lanes
+      // take p * v
+      if (w == 0 && P.has_new) {
+        const float* kd = knv + (size_t)bk * 2 * HD;
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4 qa = lds_ld16((const char*)(qk + hh * 64 + i * 8)), qb = lds_ld16((const char*)(qk + hh * 64 + i * 8 + 4));
+          const u32x4 ka = lds_ld16((const char*)(kd + hh * 64 + i * 8)), kb = lds_ld16((const char*)(kd + hh * 64 + i * 8 + 4));
+          part += __uint_as_float(qa.x) * __uint_as_float(ka.x) + __uint_as_float(qa.y) * __uint_as_float(ka.y) +
+                  __uint_as_float(qa.z) * __uint_as_float(ka.z) + __uint_as_float(qa.w) * __uint_as_float(ka.w) +
+                  __uint_as_float(qb.x) * __uint_as_float(kb.x) + __uint_as_float(qb.y) * __uint_as_float(kb.y) +
+                  __uint_as_float(qb.z) * __uint_as_float(kb.z) + __uint_as_float(qb.w) * __uint_as_float(kb.w);
+        }
+        if constexpr (LPV == 2) part += dpp_f<kDppXor1>(part);
+        const float mn = fmaxf(m1, part);
+        const float fn = fast_exp2(m1 - mn), pn = fast_exp2(part - mn);
+        l1 = l1 * fn + pn;
+        m1 = mn;
+        const float pr = vrow == 0 ? pn : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4 va = lds_ld16((const char*)(kd + HD + hh * 64 + i * 8)), vb = lds_ld16((const char*)(kd + HD + hh * 64 + i * 8 + 4));
+          const float vv[8] = {__uint_as_float(va.x), __uint_as_float(va.y), __uint_as_float(va.z), __uint_as_float(va.w),
+                               __uint_as_float(vb.x), __uint_as_float(vb.y), __uint_as_float(vb.z), __uint_as_float(vb.w)};
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o[i * 8 + u] = o[i * 8 + u] * fn + pr * vv[u];
+        }
+      }
+      mark(1);
+      // sum the rows across lanes (transposing butterfly over lane bits 5 ..
+      // log2(LPV)): lane l ends with dims (l & ~(LPV-1)) .. + 64/(64/LPV) - 1
+      // of its 64
+#pragma unroll
+      for (int k = 0; k < 32; ++k) o[k] = swap32_sum(o[k], o[k + 32]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) o[k] = swap16_sum(o[k], o[k + 16]);
+      {
+        const bool b3 = lane & 8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float keep = b3 ? o[k + 8] : o[k], send = b3 ? o[k] : o[k + 8];
+          o[k] = keep + dpp_f<kDppRor8>(send);  // lane ^ 8
+        }
+      }
+      {
+        const bool b2 = lane & 4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float keep = b2 ? o[k + 4] : o[k], send = b2 ? o[k] : o[k + 4];
+          const float s_up = b2 ? send : 0.f, s_dn = b2 ? 0.f : send;
+          o[k] = keep + dpp_f<kDppShl4>(s_up) + dpp_f<kDppShr4>(s_dn);  // lane ^ 4
+        }
+      }
+      {
+        const bool b1 = lane & 2;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float keep = b1 ? o[k + 2] : o[k], send = b1 ? o[k] : o[k + 2];
+          o[k] = keep + dpp_f<kDppXor2>(send);  // lane ^ 2
+        }
+      }
+      if constexpr (LPV == 1) {
+        const bool b0 = lane & 1;
+        const float keep = b0 ? o[1] : o[0], send = b0 ? o[0] : o[1];
+        o[0] = keep + dpp_f<kDppXor1>(send);  // lane ^ 1
+        sb[lane] = o[0];
+      } else {
+        sb[hh * 64 + (lane & ~1)] = o[0];
+        sb[hh * 64 + (lane & ~1) + 1] = o[1];
+      }
+      if (lane == 0) {
+        sb[HD] = m1;
+        sb[HD + 1] = l1;
+      }
+    } else {
     u32x4 qa_hi[NDS], qa_lo[NDS];
     {
       const int kq = 8 * lr;
@@ -2370,7 +2557,6 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     }
     mark(1);
     // wave state -> LDS
-    float* sb = stb + (pidx & 1) * stride_st + w * GM * SW;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 4 * lr + i;
@@ -2386,6 +2572,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         sb[h * SW + HD] = mrun[h];
         sb[h * SW + HD + 1] = lrun[h];
       }
+    }
     }
     if (!cbar(A, c, s.gen, lane, &s.w_bar)) return false;
     mark(2);

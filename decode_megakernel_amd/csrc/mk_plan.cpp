@@ -320,8 +320,11 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
         t.nks = T.S;
         t.part_slot = part_base[st] * 4;
         t.wait_ctr = wait;
-        t.signal_ctr = signal;
-        t.flags = kTaskSignal;
+        // only the LM head counts its completed tasks (for the greedy tokens)
+        if (st == ST_LM) {
+          t.signal_ctr = signal;
+          t.flags = kTaskSignal;
+        }
         S[c].push_back(t);
       }
       return;

@@ -124,6 +124,8 @@ SMALL_QWEN_H128 = ModelShape("small-qwen-h128", 2, 768, 8, 4, 128, 2048, 3000,
                              True, True, 1e6, 1e-6)
 SMALL_MHA_H128 = ModelShape("small-mha-h128", 2, 640, 5, 5, 128, 1792, 2000,
                             False, False, 1e4, 1e-5)
+SMALL_MHA_H64 = ModelShape("small-mha-h64", 2, 384, 6, 6, 64, 1024, 1500,
+                           True, False, 1e4, 1e-5)
 # A 2-layer model wide enough (hidden 2048, 4 K blocks; down projection 8 K
 # blocks) that row-owner tasks at batch 7 and above need several LDS input
 # windows, so the K-split tiles run on both the VALU and the MFMA path.

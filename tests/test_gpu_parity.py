@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from gpu_harness import Case, run_step, assert_step_ok, log
-from mkinputs import TINY_LLAMA, TINY_QWEN, SMALL_LLAMA_H64, SMALL_QWEN_H128, SMALL_MHA_H128
+from mkinputs import TINY_LLAMA, TINY_QWEN, SMALL_LLAMA_H64, SMALL_QWEN_H128, SMALL_MHA_H128, SMALL_MHA_H64
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,8 @@ CASES = [
     (SMALL_LLAMA_H64, [17] * 8, 2),          # batch 8: MFMA tiles, equal lengths
     (SMALL_QWEN_H128, [5, 300, 77, 1000, 2, 64, 129, 511, 3], 2),  # batch 9 ragged MFMA
     (SMALL_MHA_H128, [int(x) for x in torch.randint(1, 600, (16,), generator=torch.Generator().manual_seed(3))], 2),
+    (SMALL_MHA_H64, [0, 63, 64, 65, 300, 1], 3),  # MHA at head_dim 64: one K/V row per lane, chunk edges
+    (SMALL_MHA_H64, [int(x) for x in torch.randint(1, 400, (12,), generator=torch.Generator().manual_seed(5))], 2),
 ]
 
 
