@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the headline workload")
     ap.add_argument("--per-config-steps", type=int, default=10)
+    ap.add_argument("--no-per-op", action="store_true",
+                    help="skip the per-operation baseline beside the per-config workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling profiler byte counters) and exit")
     return ap.parse_args()
@@ -154,6 +156,112 @@ class Run:
         del self.weights, self.K, self.V
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+
+
+class PerOpEngine:
+    """The same decode step as one library call per operation (PyTorch on
+    ROCm: hipBLASLt GEMMs, elementwise, reduction and softmax kernels), on the
+    same weights and KV cache -- the per-operation engine the megakernel is
+    measured against, never used by the library.  Residual and attention in
+    fp32, GEMMs in bf16; every sequence's attention is its own set of calls."""
+
+    def __init__(self, run):
+        import torch
+        sh = run.shape
+        self.run, self.sh = run, sh
+        self.w = run.weights
+        j = torch.arange(sh.head_dim // 2, dtype=torch.float64)
+        self.freq = (sh.rope_theta ** (-2.0 * j / sh.head_dim)).to("cuda")
+
+    def _norm(self, x, w):
+        import torch
+        return x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + self.sh.rms_eps) * w.float()
+
+    def _rope(self, x, pos):
+        import torch
+        ang = pos[:, None].double() * self.freq[None, :]
+        c, s = ang.cos().float()[:, None, :], ang.sin().float()[:, None, :]
+        h = x.shape[-1] // 2
+        a, b = x[..., :h], x[..., h:]
+        return torch.cat([a * c - b * s, b * c + a * s], -1)
+
+    def step(self, tokens, positions, host_positions):
+        import torch
+        import torch.nn.functional as F
+        sh, w, run = self.sh, self.w, self.run
+        b, hd, nkv, G = tokens.numel(), sh.head_dim, sh.n_kv_heads, sh.group
+        pos = positions.long()
+        x = w["model.embed_tokens.weight"][tokens.long()].float()
+        for l in range(sh.n_layers):
+            p = f"model.layers.{l}."
+            u = self._norm(x, w[p + "input_layernorm.weight"]).bfloat16()
+            q = F.linear(u, w[p + "self_attn.q_proj.weight"]).float().view(b, sh.n_q_heads, hd)
+            k = F.linear(u, w[p + "self_attn.k_proj.weight"]).float().view(b, nkv, hd)
+            v = F.linear(u, w[p + "self_attn.v_proj.weight"]).float().view(b, nkv, hd)
+            if sh.qk_norm:
+                q = self._norm(q, w[p + "self_attn.q_norm.weight"])
+                k = self._norm(k, w[p + "self_attn.k_norm.weight"])
+            q, k = self._rope(q, pos), self._rope(k, pos)
+            ar = torch.arange(b, device="cuda")
+            run.K[l, ar, :, pos] = k.bfloat16()
+            run.V[l, ar, :, pos] = v.bfloat16()
+            outs = []
+            for i in range(b):
+                n = host_positions[i] + 1
+                Ki = run.K[l, i, :, :n].float()                     # [nkv, n, hd]
+                Vi = run.V[l, i, :, :n].float()
+                qi = q[i].view(nkv, G, hd)
+                sc = torch.matmul(qi, Ki.transpose(1, 2).contiguous()) / hd ** 0.5
+                outs.append(torch.matmul(torch.softmax(sc, -1), Vi).reshape(-1))
+            o = torch.stack(outs).bfloat16()
+            x = x + F.linear(o, w[p + "self_attn.o_proj.weight"]).float()
+            u2 = self._norm(x, w[p + "post_attention_layernorm.weight"]).bfloat16()
+            a = F.silu(F.linear(u2, w[p + "mlp.gate_proj.weight"]).float()) * F.linear(u2, w[p + "mlp.up_proj.weight"]).float()
+            x = x + F.linear(a.bfloat16(), w[p + "mlp.down_proj.weight"]).float()
+        from mkinputs import lm_head_name
+        logits = F.linear(self._norm(x, w["model.norm.weight"]).bfloat16(), w[lm_head_name(sh)]).float()
+        return torch.argmax(logits, -1).to(torch.int32)
+
+
+def per_op_baseline(run, b, warmup, steps):
+    """Time the per-operation engine on the run's weights and cache (positions
+    past the megakernel's, so the same cached rows are attended) and count its
+    kernel launches per step."""
+    import torch
+    from decode_megakernel_amd.bytes_model import step_bytes, HBM_PEAK_BYTES_PER_S
+    eng = PerOpEngine(run)
+    base = [run.ctx[i] + run.done[i] for i in range(b)]
+    tok = run.first_tok[:b].clone()
+    seq_cap = run.K.shape[3]
+    n = warmup + steps
+    if max(base) + n >= seq_cap:
+        base = [run.ctx[i] for i in range(b)]
+    hpos = [[c + k for c in base] for k in range(n)]
+    pos = [torch.tensor(hp, dtype=torch.int32, device="cuda") for hp in hpos]
+    for k in range(warmup):
+        tok = eng.step(tok, pos[k], hpos[k])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        tok = eng.step(tok, pos[warmup + k], hpos[warmup + k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launches = None
+    try:
+        from torch.profiler import profile, ProfilerActivity
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            eng.step(tok, pos[-1], hpos[-1])
+            torch.cuda.synchronize()
+        launches = int(sum(e.count for e in prof.key_averages() if e.device_type is not None and
+                           str(e.device_type).endswith("CUDA")))
+    except Exception:
+        launches = None
+    nbytes = sum(step_bytes(run.shape, [pp + 1 for pp in hpos[warmup + k]]) for k in range(steps)) / steps
+    ms = wall / steps * 1e3
+    return {"kind": "one library call per operation (PyTorch-ROCm: hipBLASLt GEMMs, elementwise, softmax)",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(b * steps / wall, 2),
+            "mbu": round(nbytes / (wall / steps) / HBM_PEAK_BYTES_PER_S, 4), "kernel_launches_per_step": launches,
+            "steps": steps}
 
 
 def summarize(ph):
@@ -276,6 +384,10 @@ def main():
                 rec["phases"].append(summarize(r2.phase(p.batch, args.warmup, k)))
             if len(rec["phases"]) == 2:
                 rec["mbu_ratio_last_to_first"] = round(rec["phases"][1]["mbu"] / rec["phases"][0]["mbu"], 4)
+            if not args.no_per_op:
+                po = per_op_baseline(r2, w2.phases[-1].batch, 2, 3)
+                po["megakernel_speedup"] = round(po["ms_per_step"] / rec["phases"][-1]["kernel_ms_mean"], 3)
+                rec["per_op_baseline"] = po
             r2.close()
             del r2
             per_config[key] = rec

@@ -16,6 +16,7 @@ STATUS_BAD_TOKEN = 1
 STATUS_BAD_POSITION = 2
 STATUS_BAD_SEQLEN = 4
 STATUS_TIMEOUT = 8
+STATUS_BAD_BLOCK = 16
 ERRORS = {-1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_OOM", -4: "MK_ERR_HIP",
           -5: "MK_ERR_PLAN", -6: "MK_ERR_TOO_LARGE"}
 
@@ -49,6 +50,12 @@ class KVCache(ctypes.Structure):
                 ("seq_cap", ctypes.c_int32)]
 
 
+class PagedKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("n_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32)]
+
+
 class PlanStats(ctypes.Structure):
     _fields_ = [("n_tasks", ctypes.c_int32), ("max_tasks_per_cu", ctypes.c_int32),
                 ("n_counters", ctypes.c_int32), ("mfma", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
@@ -59,7 +66,7 @@ class PlanStats(ctypes.Structure):
                 ("attn_slots_valid", ctypes.c_int32), ("stage_kpieces", ctypes.c_int32 * 6)]
 
 
-EXPORTS = ["mk_create", "mk_decode_step", "mk_decode_step_static", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
+EXPORTS = ["mk_create", "mk_decode_step", "mk_decode_step_paged", "mk_decode_step_static", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
            "mk_reset", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
 STAT_WORDS = 80  # per-CU trace totals, see mk_copy_trace
@@ -78,6 +85,7 @@ def lib():
     L.mk_create.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(WeightPtrs), ctypes.POINTER(vp)]
     L.mk_decode_step.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp]
     L.mk_decode_step_static.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(KVCache), vp, vp, vp]
+    L.mk_decode_step_paged.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(PagedKV), vp, vp, vp]
     L.mk_copy_hidden.argtypes = [vp, i32, vp, vp]
     L.mk_copy_state.argtypes = [vp, i32, i32, vp, vp]
     L.mk_copy_trace.argtypes = [vp, vp, ctypes.c_int64, ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
@@ -182,6 +190,21 @@ class DecodeEngine:
                 ctypes.byref(kv), logits.data_ptr(), None if next_tokens is None else next_tokens.data_ptr(),
                 _stream_handle(stream))
         _check(rc, "mk_decode_step_static" if static else "mk_decode_step")
+
+    def step_paged(self, tokens, positions, seq_lens, k_pool, v_pool, block_table, logits, next_tokens=None,
+                   stream=None, batch=None):
+        """Enqueue one decode step over a paged KV cache: k_pool, v_pool bf16
+        [L][n_blocks][n_kv][block_size][hd]; block_table int32 [>= batch, max_blocks]
+        (contiguous rows)."""
+        b = int(tokens.numel()) if batch is None else int(batch)
+        assert block_table.is_contiguous() and block_table.dtype.itemsize == 4
+        kv = PagedKV(k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(), int(k_pool.shape[1]),
+                     int(k_pool.shape[3]), int(block_table.shape[1]))
+        rc = lib().mk_decode_step_paged(self.handle, b, tokens.data_ptr(), positions.data_ptr(),
+                                        seq_lens.data_ptr(), ctypes.byref(kv), logits.data_ptr(),
+                                        None if next_tokens is None else next_tokens.data_ptr(),
+                                        _stream_handle(stream))
+        _check(rc, "mk_decode_step_paged")
 
     def copy_hidden(self, batch: int, out, stream=None):
         _check(lib().mk_copy_hidden(self.handle, int(batch), out.data_ptr(), _stream_handle(stream)),

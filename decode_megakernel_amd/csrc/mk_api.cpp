@@ -486,15 +486,28 @@ static size_t part_bytes_of(const mk_handle* h, const GraphDev& g) {
 
 // Checks and kernel arguments shared by both step entry points; the
 // workspace pointers are the handle's own.
+// The KV cache of a step: contiguous rows per sequence, or paged blocks.
+struct KVDesc {
+  void *k = nullptr, *v = nullptr;
+  int bcap = 0, scap = 0;            // contiguous: sequence rows and positions per row
+  const int32_t* btab = nullptr;     // paged: block table, NULL for contiguous
+  int bt_stride = 0, bsize = 0, nblocks = 0;
+};
+
 static int step_args(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
-                     const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out, int32_t* next_tokens_out,
+                     const int32_t* seq_lens, const KVDesc* kv, float* logits_out, int32_t* next_tokens_out,
                      DevArgs& A, GraphDev** gout) {
   if (!h) return MK_ERR_INVALID_ARG;
   if (batch < 0 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
   if (batch == 0) return MK_OK;
   if (!tokens || !positions || !seq_lens || !kv || !kv->k || !kv->v || !logits_out) return MK_ERR_INVALID_ARG;
-  if (kv->batch_cap < batch || kv->seq_cap < 1) return MK_ERR_INVALID_ARG;
-  if ((long long)h->cfg.n_kv_heads * batch * kv->seq_cap >= (1LL << 31)) return MK_ERR_UNSUPPORTED;
+  if (kv->btab) {
+    // a chunk of cached rows (at most 64) must span at most two blocks
+    if (kv->bsize < 64 || kv->nblocks < 1 || kv->bt_stride < 1) return MK_ERR_INVALID_ARG;
+  } else if (kv->bcap < batch || kv->scap < 1) {
+    return MK_ERR_INVALID_ARG;
+  }
+  if ((long long)h->cfg.n_kv_heads * batch * kv->scap >= (1LL << 31)) return MK_ERR_UNSUPPORTED;
   auto git = h->graphs.find(batch);
   if (git == h->graphs.end()) return MK_ERR_INVALID_ARG;  // every batch 1..max_batch is built by mk_create
   GraphDev* g = &git->second;
@@ -521,8 +534,12 @@ static int step_args(mk_handle* h, int32_t batch, const int32_t* tokens, const i
   A.final_norm = h->final_norm;
   A.kc = (uint16_t*)kv->k;
   A.vc = (uint16_t*)kv->v;
-  A.kv_bcap = kv->batch_cap;
-  A.kv_scap = kv->seq_cap;
+  A.kv_bcap = kv->bcap;
+  A.kv_scap = kv->scap;
+  A.btab = kv->btab;
+  A.bt_stride = kv->bt_stride;
+  A.bsize = kv->bsize;
+  A.nblocks = kv->nblocks;
   A.tokens = tokens;
   A.positions = positions;
   A.seq_lens = seq_lens;
@@ -568,12 +585,46 @@ static int step_args(mk_handle* h, int32_t batch, const int32_t* tokens, const i
   return MK_OK;
 }
 
+static KVDesc contiguous(const mk_kv_cache* kv) {
+  KVDesc d;
+  if (kv) {
+    d.k = kv->k;
+    d.v = kv->v;
+    d.bcap = kv->batch_cap;
+    d.scap = kv->seq_cap;
+  }
+  return d;
+}
+
 int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
                    const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out, int32_t* next_tokens_out,
                    void* stream) {
   DevArgs A;
   GraphDev* g = nullptr;
-  int rc = step_args(h, batch, tokens, positions, seq_lens, kv, logits_out, next_tokens_out, A, &g);
+  const KVDesc d = contiguous(kv);
+  int rc = step_args(h, batch, tokens, positions, seq_lens, kv ? &d : nullptr, logits_out, next_tokens_out, A, &g);
+  if (rc || batch == 0) return rc;
+  if (launch_step(A, (hipStream_t)stream, h->coop != 0) != hipSuccess) return MK_ERR_HIP;
+  h->rowtag = A.rowtag;
+  h->step += 1;
+  return MK_OK;
+}
+
+int mk_decode_step_paged(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                         const int32_t* seq_lens, const mk_paged_kv* kv, float* logits_out, int32_t* next_tokens_out,
+                         void* stream) {
+  if (!kv || !kv->block_table) return MK_ERR_INVALID_ARG;
+  KVDesc d;
+  d.k = kv->k;
+  d.v = kv->v;
+  d.btab = kv->block_table;
+  d.bt_stride = kv->max_blocks_per_seq;
+  d.bsize = kv->block_size;
+  d.nblocks = kv->n_blocks;
+  d.scap = kv->max_blocks_per_seq * kv->block_size;  // positions a sequence can address
+  DevArgs A;
+  GraphDev* g = nullptr;
+  int rc = step_args(h, batch, tokens, positions, seq_lens, &d, logits_out, next_tokens_out, A, &g);
   if (rc || batch == 0) return rc;
   if (launch_step(A, (hipStream_t)stream, h->coop != 0) != hipSuccess) return MK_ERR_HIP;
   h->rowtag = A.rowtag;
@@ -586,7 +637,8 @@ int mk_decode_step_static(mk_handle* h, int32_t batch, const int32_t* tokens, co
                           int32_t* next_tokens_out, void* stream) {
   DevArgs A;
   GraphDev* g = nullptr;
-  int rc = step_args(h, batch, tokens, positions, seq_lens, kv, logits_out, next_tokens_out, A, &g);
+  const KVDesc d = contiguous(kv);
+  int rc = step_args(h, batch, tokens, positions, seq_lens, kv ? &d : nullptr, logits_out, next_tokens_out, A, &g);
   if (rc || batch == 0) return rc;
   if (h->static_bytes > kStaticScratchBytes) return MK_ERR_TOO_LARGE;
   if (!h->sbase) return MK_ERR_HIP;

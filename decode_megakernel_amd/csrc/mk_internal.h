@@ -173,6 +173,11 @@ struct DevArgs {
   int32_t trace_cap;
   int32_t attn_pad;         // attention partition: empty rows ahead of each segment (upper bound)
   float* dump;              // optional caller buffer [L+1][bcap][d]: residual stream, tag bit cleared (NULL = off)
+  // paged KV cache: K / V pools [L][nblocks][nkv][bsize][hd]; position p of
+  // sequence i lives in block btab[i * bt_stride + p / bsize] at row p % bsize
+  // (btab NULL: rows [L][kv_bcap][nkv][kv_scap][hd])
+  const int32_t* btab;
+  int32_t bt_stride, bsize, nblocks;
 };
 
 // Host planner --------------------------------------------------------------

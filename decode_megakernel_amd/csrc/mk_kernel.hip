@@ -86,6 +86,7 @@ __device__ __forceinline__ TaskP uni(TaskP p) {
   return (TaskP)(((unsigned long long)hi << 32) | lo);
 }
 constexpr uint32_t kStatusTimeout = 8u;
+constexpr uint32_t kStatusBadBlock = 16u;
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
@@ -599,6 +600,33 @@ __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rp
   return true;
 }
 
+// ---- KV-cache rows.  Element offset (in head_dim units) of position p of
+// sequence i, KV head g, layer l: contiguous rows per sequence, or a block of
+// a paged pool looked up in the block table (an id outside the pool is
+// clamped and raises MK_STATUS_BAD_BLOCK).
+// The block table is read-only during a step.  UNIFORM = the arguments are
+// the same on every lane: the entry is then read through the scalar cache,
+// so the lookup never waits behind the loader's streaming loads.
+template <bool UNIFORM>
+__device__ __forceinline__ int kv_block(DArgs A, int i, int lb) {
+  const size_t idx = (size_t)i * A->bt_stride + lb;
+  int blk = UNIFORM ? __builtin_amdgcn_readfirstlane(as_const(A->btab)[idx]) : A->btab[idx];
+  if ((unsigned)blk >= (unsigned)A->nblocks) {
+    atomicOr(A->status, kStatusBadBlock);
+    blk = blk < 0 ? 0 : A->nblocks - 1;
+  }
+  return blk;
+}
+template <bool UNIFORM>
+__device__ __forceinline__ size_t kv_row(DArgs A, int l, int i, int g, int p) {
+  if (A->btab) {
+    const int lb = p / A->bsize;
+    const int blk = kv_block<UNIFORM>(A, i, lb);
+    return (((size_t)l * A->nblocks + blk) * A->nkv + g) * A->bsize + (p - lb * A->bsize);
+  }
+  return (((size_t)l * A->kv_bcap + i) * A->nkv + g) * A->kv_scap + p;
+}
+
 // ================================================================ loader
 // The loader waves move weight tiles and cached K/V rows into the LDS ring
 // with direct-to-LDS loads (global_load_lds_dwordx4): no data registers, up
@@ -693,16 +721,26 @@ __device__ __forceinline__ void dma_gemv_chunk(DArgs A, const RowBase& rb, int k
 // (one query head per KV head: the VALU attention tiles) row r's 16-byte
 // groups are stored rotated by r & 7, so LDS position p of row r holds group
 // (p + (r & 7)) mod (groups per row).
-template <int HD>
-__device__ __forceinline__ void dma_attn_chunk(DArgs A, const uint16_t* kbase, const uint16_t* vbase, int rows, int lane,
-                                               char* dst, bool rot) {
+template <int HD, bool PAGED>
+__device__ __forceinline__ void dma_attn_chunk(DArgs A, const uint16_t* k0, const uint16_t* v0, const uint16_t* k1,
+                                               const uint16_t* v1, int split, int rows, int lane, char* dst, bool rot) {
+  // rows [0, split) from k0 / v0, rows [split, rows) from k1 / v1 (a paged
+  // chunk that crosses into the sequence's next block); contiguous caches
+  // pass split = rows and keep one base per lane (per-lane address work runs
+  // on the compute waves' SIMDs)
   constexpr int LPR = HD / 8, RP = 64 / LPR;
   const int pos = lane % LPR;
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
     const int rl = (j & 7) * RP + lane / LPR;
     const int e = (rot ? ((pos + (rl & 7)) & (LPR - 1)) : pos) * 8;
-    const uint16_t* src = (j < 8 ? kbase : vbase) + (size_t)rl * HD + e;
+    const uint16_t* src;
+    if constexpr (PAGED) {
+      const bool sec = rl >= split;
+      src = (j < 8 ? (sec ? k1 : k0) : (sec ? v1 : v0)) + (uint32_t)((sec ? rl - split : rl) * HD + e);
+    } else {
+      src = (j < 8 ? k0 : v0) + (uint32_t)(rl * HD + e);
+    }
     dma16(rl < rows ? (const void*)src : (const void*)A->zero, dst + j * 1024);
   }
 }
@@ -809,14 +847,27 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
       Piece P;
       int pbase = qbase;
       while (next_piece_r(sl, A->b, A->nkv, rpc, pad, pos, hi, P)) {
-        const size_t head = (((size_t)t.layer * A->kv_bcap + P.i) * A->nkv + P.g) * A->kv_scap;
         for (int ch = R.q - pbase; ch < P.nch; ch += kLoaderWaves) {
           if (!ring_acquire(A, c, R, lane)) return;
-          const size_t row0 = (head + P.j0 + (size_t)ch * rpc) * A->hd;
+          const int p0 = P.j0 + ch * rpc;
           const int rows = min(rpc, P.ncached - ch * rpc);
           char* dst = ring + (size_t)R.slot * kSlotBytes;
-          if (A->hd == 128) dma_attn_chunk<128>(A, A->kc + row0, A->vc + row0, rows, lane, dst, A->G == 1);
-          else dma_attn_chunk<64>(A, A->kc + row0, A->vc + row0, rows, lane, dst, A->G == 1);
+          const size_t r0 = kv_row<true>(A, t.layer, P.i, P.g, p0) * A->hd;
+          if (A->btab) {
+            // a chunk (at most 64 rows, blocks at least 64 positions) spans at most two blocks
+            const int lb = p0 / A->bsize;
+            const int split = min(rows, (lb + 1) * A->bsize - p0);
+            const size_t r1 = split < rows ? kv_row<true>(A, t.layer, P.i, P.g, (lb + 1) * A->bsize) * A->hd : r0;
+            if (A->hd == 128)
+              dma_attn_chunk<128, true>(A, A->kc + r0, A->vc + r0, A->kc + r1, A->vc + r1, split, rows, lane, dst, A->G == 1);
+            else
+              dma_attn_chunk<64, true>(A, A->kc + r0, A->vc + r0, A->kc + r1, A->vc + r1, split, rows, lane, dst, A->G == 1);
+          } else {
+            if (A->hd == 128)
+              dma_attn_chunk<128, false>(A, A->kc + r0, A->vc + r0, nullptr, nullptr, rows, rows, lane, dst, A->G == 1);
+            else
+              dma_attn_chunk<64, false>(A, A->kc + r0, A->vc + r0, nullptr, nullptr, rows, rows, lane, dst, A->G == 1);
+          }
           ring_issued(A, c, R, lane);
         }
         pbase += P.nch;
@@ -2208,7 +2259,7 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         const u32x4 kb = {pack_bf2(x8[0], x8[1]), pack_bf2(x8[2], x8[3]), pack_bf2(x8[4], x8[5]), pack_bf2(x8[6], x8[7])};
         const u32x4 vb = {pack_bf2(__uint_as_float(v0.x), __uint_as_float(v0.y)), pack_bf2(__uint_as_float(v0.z), __uint_as_float(v0.w)),
                           pack_bf2(__uint_as_float(v1.x), __uint_as_float(v1.y)), pack_bf2(__uint_as_float(v1.z), __uint_as_float(v1.w))};
-        const size_t slot_row = ((((size_t)l * A->kv_bcap + pi) * A->nkv + pg) * A->kv_scap + pp) * HD + e0;
+        const size_t slot_row = kv_row<false>(A, l, pi, pg, pp) * HD + e0;
         *(u32x4*)(A->kc + slot_row) = kb;
         *(u32x4*)(A->vc + slot_row) = vb;
         float kf[8], vf[8];

@@ -46,6 +46,8 @@ extern "C" {
 #define MK_STATUS_BAD_TOKEN 1u     /* tokens[i] outside [0, vocab)                  */
 #define MK_STATUS_BAD_POSITION 2u  /* positions[i] outside [0, min(max_seq, seq_cap)) */
 #define MK_STATUS_BAD_SEQLEN 4u    /* seq_lens[i] != positions[i] + 1               */
+#define MK_STATUS_BAD_BLOCK 16u    /* mk_decode_step_paged: a block-table entry outside
+                                      [0, n_blocks) (clamped) */
 #define MK_STATUS_TIMEOUT 8u       /* a dependency wait exceeded the spin limit; the
                                       step was abandoned, later steps give up their waits
                                       too, and this bit stays reported until mk_reset */
@@ -161,6 +163,37 @@ int mk_decode_step(mk_handle* h, int32_t batch, const int32_t* tokens, const int
 int mk_decode_step_static(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
                           const int32_t* seq_lens, const mk_kv_cache* kv, float* logits_out,
                           int32_t* next_tokens_out, void* stream);
+
+/* Paged KV cache (the Cohere engine digest, "Integration": compatible with
+ * continuous batching and paged attention).  DEVICE pools, caller-owned:
+ *   k, v          bf16 [n_layers][n_blocks][n_kv_heads][block_size][head_dim];
+ *   block_table   int32 [batch][max_blocks_per_seq]: entry j of row i is the
+ *                 pool block holding positions j*block_size .. +block_size-1
+ *                 of the sequence in batch slot i (the same block index in
+ *                 every layer's pool);
+ *   block_size    positions per block, >= 64;
+ *   n_blocks      blocks per layer pool (entries outside [0, n_blocks) are
+ *                 clamped and raise MK_STATUS_BAD_BLOCK).
+ * Positions must be < max_blocks_per_seq * block_size (else clamped,
+ * MK_STATUS_BAD_POSITION).  Sequences join and leave between steps by
+ * rewriting block-table rows: slot i of a step is whatever sequence the
+ * caller puts there. */
+typedef struct {
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  int32_t n_blocks;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+} mk_paged_kv;
+
+/* mk_decode_step over a paged KV cache: the same step, kernel and schedules,
+ * with every cached K/V row and the new row addressed through the block
+ * table.  Results are identical to mk_decode_step on a contiguous cache with
+ * the same rows. */
+int mk_decode_step_paged(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
+                         const int32_t* seq_lens, const mk_paged_kv* kv, float* logits_out,
+                         int32_t* next_tokens_out, void* stream);
 
 /* Copy the residual stream of the last step, enqueued on `stream` (the
  * per-layer hidden states the mid-state oracle checks: the ForgeMegakernel

@@ -28,6 +28,8 @@ from decode_megakernel_amd.binding import DecodeEngine, STATE_HMID
 from mkinputs import make_weights, make_kv_cache, make_kv_layer, bf16_bits, draw_tokens
 
 TOL = 1e-2
+# mean absolute error of the greedy token's log-probability against float64
+LOGPROB_TOL = 1e-2
 
 
 def rel_l2(g, r) -> float:
@@ -207,9 +209,19 @@ def run_step(case: Case, check_kv_invariant=True, compare=True, batch=None):
                 tok_ok = tok_ok and int(g_next[i]) == ref["tokens"][i]
             else:
                 near_ties += 1
+        # log-probability the decoder assigns to the token it goes on with,
+        # against the float64 forward pass (the pages' "mean log-probability
+        # error"), per sequence
+        lp_err = []
+        for i in range(b):
+            t = int(g_next[i])
+            lg, lr = g_logits[i], ref["logits"][i]
+            lp_g = lg[t] - (lg.max() + np.log(np.sum(np.exp(lg - lg.max()))))
+            lp_r = lr[t] - (lr.max() + np.log(np.sum(np.exp(lr - lr.max()))))
+            lp_err.append(abs(float(lp_g - lp_r)))
         out.update(h0_exact=bool(h0_exact), hidden_err=hid_err, hmid_err=hmid_err, logits_err=log_err, k_err=k_err,
                    v_err=v_err, tokens_oracle_ok=bool(tok_ok), near_ties=near_ties,
-                   hidden_err_last_layer=max(hid[-1]))
+                   hidden_err_last_layer=max(hid[-1]), logprob_err=lp_err)
     case.tokens[:b] = [int(t) for t in g_next]
     case.step_idx += 1
     return out

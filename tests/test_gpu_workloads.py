@@ -22,7 +22,9 @@ import gc
 import pytest
 import torch
 
-from gpu_harness import Case, run_step, assert_step_ok, log, TOL
+import json
+
+from gpu_harness import Case, run_step, assert_step_ok, log, TOL, LOGPROB_TOL
 from mkinputs import WORKLOADS, draw_contexts, kv_capacity
 
 pytestmark = pytest.mark.gpu
@@ -40,13 +42,20 @@ def _contexts(wl, batch):
 
 def _run(case, batches, tag):
     worst = {}
+    lp = []
     for s, b in enumerate(batches):
         r = run_step(case, check_kv_invariant=True, batch=b)
+        lp += r["logprob_err"]
         log(f"  {tag} step {s} (batch {b}): {r}")
         assert_step_ok(r)
         for k in ("hidden_err", "hmid_err", "logits_err", "k_err", "v_err"):
             worst[k] = max(worst.get(k, 0.0), r[k])
     log(f"  {tag} worst over {len(batches)} steps: {worst}")
+    # mean absolute log-probability error of the greedy tokens against float64
+    rec = {"workload": tag, "tokens": len(lp), "mean_logprob_err": sum(lp) / len(lp), "max_logprob_err": max(lp),
+           **{f"max_{k}": v for k, v in worst.items()}}
+    log("LOGPROB " + json.dumps(rec))
+    assert rec["mean_logprob_err"] <= LOGPROB_TOL, rec
     return worst
 
 
