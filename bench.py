@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--per-config-steps", type=int, default=10)
     ap.add_argument("--no-per-op", action="store_true",
                     help="skip the per-operation baseline beside the per-config workloads")
+    ap.add_argument("--context-sweep", action="store_true",
+                    help="Qwen3-8B-shaped model at batch 1 and 8 over contexts 64-4096, with and without "
+                         "context routing (mk_set_context_bound); prints one JSON line and exits")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling profiler byte counters) and exit")
     return ap.parse_args()
@@ -264,6 +267,54 @@ def per_op_baseline(run, b, warmup, steps):
             "steps": steps}
 
 
+def context_sweep(steps=10, warmup=4):
+    """The pages' context-length sweep (Qwen3-8B shape, contexts 64-4096):
+    kernel ms and MBU per (batch, context), with the step routed to its
+    context bucket (mk_set_context_bound) and without."""
+    import torch
+    from mkinputs import QWEN3_8B, make_weights, make_kv_cache, draw_tokens
+    from decode_megakernel_amd.binding import DecodeEngine
+    from decode_megakernel_amd.bytes_model import step_bytes, HBM_PEAK_BYTES_PER_S
+    sh = QWEN3_8B
+    w = make_weights(sh, 2001, device="cuda")
+    rows = []
+    for b in (1, 8):
+        for S in (64, 128, 256, 512, 1024, 2048, 4096):
+            ctx = [S] * b
+            cap = S + 2 * (warmup + steps) + 1
+            K, V = make_kv_cache(sh, 2001, ctx, b, cap, device="cuda")
+            rec = {"batch": b, "context": S}
+            for routed in (False, True):
+                eng = DecodeEngine(sh, w, max_batch=b, max_seq=cap)
+                if routed:
+                    eng.set_context_bound(S + warmup + steps + 1)
+                tok = torch.tensor(draw_tokens(1, b, sh.vocab), dtype=torch.int32, device="cuda")
+                logits = torch.empty((b, sh.vocab), dtype=torch.float32, device="cuda")
+                times, nbytes = [], []
+                for k in range(warmup + steps):
+                    pos = torch.tensor([c + k for c in ctx], dtype=torch.int32, device="cuda")
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    eng.step(tok, pos, pos + 1, K, V, logits, tok)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    if k >= warmup:
+                        times.append(e0.elapsed_time(e1) * 1e-3)
+                        nbytes.append(step_bytes(sh, [c + k + 1 for c in ctx]))
+                if eng.status():
+                    raise RuntimeError("device status during the context sweep")
+                eng.close()
+                key = "routed" if routed else "default"
+                rec[key + "_ms"] = round(sum(times) / len(times) * 1e3, 4)
+                rec[key + "_mbu"] = round(sum(nbytes) / sum(times) / HBM_PEAK_BYTES_PER_S, 4)
+            rows.append(rec)
+            print("# " + json.dumps(rec), file=sys.stderr, flush=True)
+            del K, V
+            torch.cuda.empty_cache()
+    print(json.dumps({"context_sweep": "qwen3-8b (36 layers, hidden 4096, 32/8 heads, head_dim 128, QK-norm, untied)",
+                      "rows": rows}), flush=True)
+
+
 def summarize(ph):
     from decode_megakernel_amd.bytes_model import HBM_PEAK_BYTES_PER_S
     ks = sum(ph["per_step_s"])
@@ -352,6 +403,9 @@ def main():
     import torch
     if args.copy_probe:
         copy_probe()
+        return
+    if args.context_sweep:
+        context_sweep()
         return
     from mkinputs import WORKLOADS
     from decode_megakernel_amd.bytes_model import HBM_PEAK_BYTES_PER_S

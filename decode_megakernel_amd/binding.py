@@ -67,7 +67,7 @@ class PlanStats(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_decode_step", "mk_decode_step_paged", "mk_decode_step_static", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
-           "mk_reset", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan"]
+           "mk_reset", "mk_set_context_bound", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
 STAT_WORDS = 80  # per-CU trace totals, see mk_copy_trace
 
@@ -92,6 +92,7 @@ def lib():
     L.mk_get_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.mk_reset.argtypes = [vp, vp]
     L.mk_set_midstate_dump.argtypes = [vp, vp]
+    L.mk_set_context_bound.argtypes = [vp, i32]
     L.mk_destroy.argtypes = [vp]
     L.mk_error_string.argtypes = [ctypes.c_int]
     L.mk_error_string.restype = ctypes.c_char_p
@@ -247,6 +248,11 @@ class DecodeEngine:
         s = ctypes.c_uint32()
         _check(lib().mk_get_status(self.handle, _stream_handle(stream), ctypes.byref(s)), "mk_get_status")
         return int(s.value)
+
+    def set_context_bound(self, max_seq_len: int):
+        """Route later steps to the attention partition of their context bucket
+        (0: no bound)."""
+        _check(lib().mk_set_context_bound(self.handle, int(max_seq_len)), "mk_set_context_bound")
 
     def set_midstate_dump(self, out):
         """Every later step also writes its residual stream into `out` (a CUDA

@@ -84,6 +84,9 @@ struct mk_handle {
   uint64_t* trace = nullptr;   // MK_TRACE=<tasks per CU>: per-task timestamps + per-CU wait totals
   int trace_cap = 0;
   int attn_pad = 0;            // attention partition: empty rows ahead of each segment (upper bound)
+  int attn_min_rows = 32;      // attention partition: rows a CU takes at least
+  int ctx_bound = 0;           // caller's bound on seq_lens (mk_set_context_bound), 0 = none
+  bool knob_pad = false, knob_min_rows = false;  // partition fixed from the environment
 };
 
 extern "C" {
@@ -386,6 +389,9 @@ int mk_create(const mk_model_cfg* cfg, const mk_weight_ptrs* w, mk_handle** out)
   // rows' worth of time (512 rows at head_dim 128; the kernel caps the pad
   // at half a CU's rows).
   h->attn_pad = std::max(0, env_int("MK_ATTN_PAD", (256 << 10) / (4 * cfg->head_dim)));
+  h->attn_min_rows = std::max(1, env_int("MK_ATTN_MIN_ROWS", 32));
+  h->knob_pad = getenv("MK_ATTN_PAD") && *getenv("MK_ATTN_PAD");
+  h->knob_min_rows = getenv("MK_ATTN_MIN_ROWS") && *getenv("MK_ATTN_MIN_ROWS");
   h->trace_cap = env_int("MK_TRACE", 0);
   if (h->trace_cap > 0) {
     size_t tb = ((size_t)h->ncu * h->trace_cap * 4 + (size_t)h->ncu * kStatWords) * 8;
@@ -494,6 +500,28 @@ struct KVDesc {
   int bt_stride = 0, bsize = 0, nblocks = 0;
 };
 
+// Context routing: with a context bound declared by the caller, the attention
+// partition of a step takes the parameters measured best for its (batch
+// class, context bucket) on a Qwen3-8B-shaped model (head_dim 128, 8 KV
+// heads) swept over contexts 64-4096: (empty rows ahead of each segment in
+// units of 256 KB of K/V rows, rows a CU takes at least).  Without a bound
+// (or with the partition fixed from the environment) the defaults apply.
+static void route_attention(const mk_handle* h, int batch, DevArgs& A) {
+  if (h->ctx_bound <= 0) return;
+  struct Route {
+    int max_ctx;
+    int pad_quarters;  // pad = pad_quarters / 4 x 256 KB of K/V rows
+    int min_rows;
+  };
+  static const Route small_b[] = {{128, 4, 128}, {512, 1, 8}, {2048, 0, 8}, {1 << 30, 0, 32}};
+  static const Route large_b[] = {{128, 4, 8}, {512, 4, 32}, {2048, 0, 128}, {1 << 30, 0, 128}};
+  const Route* tab = batch >= 8 ? large_b : small_b;
+  int k = 0;
+  while (h->ctx_bound > tab[k].max_ctx) ++k;
+  if (!h->knob_pad) A.attn_pad = tab[k].pad_quarters * ((256 << 10) / (4 * h->cfg.head_dim)) / 4;
+  if (!h->knob_min_rows) A.attn_min_rows = tab[k].min_rows;
+}
+
 static int step_args(mk_handle* h, int32_t batch, const int32_t* tokens, const int32_t* positions,
                      const int32_t* seq_lens, const KVDesc* kv, float* logits_out, int32_t* next_tokens_out,
                      DevArgs& A, GraphDev** gout) {
@@ -581,6 +609,8 @@ static int step_args(mk_handle* h, int32_t batch, const int32_t* tokens, const i
   A.trace = h->trace;
   A.trace_cap = h->trace_cap;
   A.attn_pad = h->attn_pad;
+  A.attn_min_rows = h->attn_min_rows;
+  route_attention(h, batch, A);
   A.dump = h->dump;
   return MK_OK;
 }
@@ -733,6 +763,12 @@ int mk_reset(mk_handle* h, void* stream) {
   ok = ok && hipMemset(h->d_part, 0, h->part_bytes) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   return ok ? MK_OK : MK_ERR_HIP;
+}
+
+int mk_set_context_bound(mk_handle* h, int32_t max_seq_len) {
+  if (!h || max_seq_len < 0) return MK_ERR_INVALID_ARG;
+  h->ctx_bound = max_seq_len;
+  return MK_OK;
 }
 
 int mk_set_midstate_dump(mk_handle* h, float* hidden_out) {

@@ -172,6 +172,7 @@ struct DevArgs {
   uint64_t* trace;          // optional per-task timestamps [ncu][trace_cap][4], NULL = off
   int32_t trace_cap;
   int32_t attn_pad;         // attention partition: empty rows ahead of each segment (upper bound)
+  int32_t attn_min_rows;    // attention partition: rows a CU takes at least
   float* dump;              // optional caller buffer [L+1][bcap][d]: residual stream, tag bit cleared (NULL = off)
   // paged KV cache: K / V pools [L][nblocks][nkv][bsize][hd]; position p of
   // sequence i lives in block btab[i * bt_stride + p / bsize] at row p % bsize

@@ -522,11 +522,10 @@ __device__ __forceinline__ int cu_of(long long x, long long W, int ncu) {
 }
 
 // CUs that attention's rows are split over: every CU, except that a CU
-// takes at least kAttnMinRows rows, so that very short contexts are not cut
+// takes at least attn_min_rows rows, so that very short contexts are not cut
 // into many tiny pieces whose partials must all be merged.
-constexpr int kAttnMinRows = 32;
-__device__ __forceinline__ int attn_ncu(long long W, int ncu) {
-  const long long n = (W + kAttnMinRows - 1) / kAttnMinRows;
+__device__ __forceinline__ int attn_ncu(long long W, int ncu, int min_rows) {
+  const long long n = (W + min_rows - 1) / min_rows;
   return n < 1 ? 1 : (n > ncu ? ncu : (int)n);
 }
 // Attention works in CU slots: the schedule numbers first the CUs its layer's
@@ -537,7 +536,7 @@ __device__ __forceinline__ int attn_slot(DArgs A, int l, int cu) {
   return as_const(A->attn_map)[(size_t)l * (A->ncu + 1) + cu];
 }
 __device__ __forceinline__ int attn_nacu(DArgs A, int l, long long W) {
-  int n = attn_ncu(W, A->ncu);
+  int n = attn_ncu(W, A->ncu, A->attn_min_rows);
   const int cap = as_const(A->attn_map)[(size_t)l * (A->ncu + 1) + A->ncu];
   if (cap > 0 && n > cap && (W + cap - 1) / cap <= kAttnCapRows) n = cap;
   return n;

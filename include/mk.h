@@ -264,6 +264,16 @@ int mk_get_status(mk_handle* h, void* stream, uint32_t* status);
  * calling mk_decode_step again with the same buffers. */
 int mk_reset(mk_handle* h, void* stream);
 
+/* Context routing (the ForgeMegakernel summary, "5.3 Serving experiment" and
+ * its Figure 5: kernels carry a batch size and a context bound, and requests
+ * are routed among them by context length).  Declares that every later step
+ * has seq_lens[i] <= max_seq_len (0 = no bound, the default): the step then
+ * runs the attention partition tuned for its (batch class, context bucket)
+ * -- buckets up to 128, 512, 2048 positions and beyond, batch classes below 8
+ * and from 8.  The schedules and results do not depend on the bound (a
+ * longer sequence is still correct, only the partition may be a poorer fit). */
+int mk_set_context_bound(mk_handle* h, int32_t max_seq_len);
+
 /* Mid-state dump: while set, every step also writes its residual stream
  * (the values mk_copy_hidden returns) into hidden_out, a DEVICE buffer the
  * caller owns, layout [n_layers+1][max_batch][hidden] float (entry l = input

@@ -88,6 +88,9 @@ LLAMA3_8B = ModelShape("llama3-8b", 32, 4096, 32, 8, 128, 14336, 128256,
                        False, False, 5e5, 1e-5)
 LLAMA2_13B = ModelShape("llama2-13b", 40, 5120, 40, 40, 128, 13824, 32000,
                         False, False, 1e4, 1e-5)
+# the model of the pages' context-length sweep (Qwen3-8B: QK-norm, untied)
+QWEN3_8B = ModelShape("qwen3-8b", 36, 4096, 32, 8, 128, 12288, 151936,
+                      False, True, 1e6, 1e-6)
 
 WORKLOADS = {
     "smollm2-135m-b1": Workload(

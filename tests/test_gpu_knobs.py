@@ -51,3 +51,19 @@ def test_knob_parity(monkeypatch, env, shape, contexts):
             assert_step_ok(r)
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("bound,ctx", [(64, [3, 40, 1, 60]), (400, [100, 7, 250]), (3000, [5, 300, 77, 1000, 2, 64, 129, 511, 3])],
+                         ids=["bound64-b4", "bound400-b3", "bound3000-b9"])
+def test_context_routing_parity(bound, ctx):
+    """Steps routed to a context bucket (mk_set_context_bound) match the oracle."""
+    log(f"context bound {bound} contexts {ctx}")
+    case = Case(SMALL_MHA_H128 if len(ctx) < 9 else SMALL_LLAMA_H64, ctx, 2, seed=2025)
+    case.engine.set_context_bound(bound)
+    try:
+        for s in range(2):
+            r = run_step(case)
+            log(f"  step {s}: {r}")
+            assert_step_ok(r)
+    finally:
+        case.close()
