@@ -56,6 +56,11 @@ class PagedKV(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32)]
 
 
+class TaskInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("type", "stage", "layer", "row0", "nsub", "k0", "k1", "ks", "nks",
+                                              "group", "part_slot", "nchunks", "flags")]
+
+
 class PlanStats(ctypes.Structure):
     _fields_ = [("n_tasks", ctypes.c_int32), ("max_tasks_per_cu", ctypes.c_int32),
                 ("n_counters", ctypes.c_int32), ("mfma", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
@@ -67,7 +72,7 @@ class PlanStats(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_decode_step", "mk_decode_step_paged", "mk_decode_step_static", "mk_copy_hidden", "mk_copy_state", "mk_copy_trace", "mk_get_status",
-           "mk_reset", "mk_set_context_bound", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan"]
+           "mk_reset", "mk_set_context_bound", "mk_set_midstate_dump", "mk_destroy", "mk_error_string", "mk_plan", "mk_plan_streams"]
 STATE_HIDDEN, STATE_HMID, STATE_QKV, STATE_ATTN, STATE_ACT = 0, 1, 2, 3, 4
 STAT_WORDS = 80  # per-CU trace totals, see mk_copy_trace
 
@@ -97,6 +102,8 @@ def lib():
     L.mk_error_string.argtypes = [ctypes.c_int]
     L.mk_error_string.restype = ctypes.c_char_p
     L.mk_plan.argtypes = [ctypes.POINTER(ModelCfg), i32, i32, ctypes.POINTER(PlanStats)]
+    L.mk_plan_streams.argtypes = [ctypes.POINTER(ModelCfg), i32, i32, ctypes.POINTER(TaskInfo), i32,
+                                  ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     for name in EXPORTS:
         if name != "mk_error_string":
             getattr(L, name).restype = ctypes.c_int
@@ -130,6 +137,25 @@ def plan(shape, batch: int, n_cu: int = 256, max_batch: int = 16, max_seq: int =
 def torch_float32():
     import torch
     return torch.float32
+
+
+def plan_streams(shape, batch: int, n_cu: int, max_batch: int = 16, max_seq: int = 8192):
+    """The per-CU instruction streams (host only): (list of per-CU lists of task
+    dicts, attention slot map [n_layers][n_cu + 1])."""
+    cfg = model_cfg(shape, max_batch, max_seq)
+    n = ctypes.c_int32()
+    offs = (ctypes.c_int32 * (n_cu + 1))()
+    rc = lib().mk_plan_streams(ctypes.byref(cfg), int(batch), int(n_cu), None, 0, offs, None, ctypes.byref(n))
+    if rc != MK_OK and n.value <= 0:
+        _check(rc, "mk_plan_streams")
+    tasks = (TaskInfo * n.value)()
+    amap = (ctypes.c_int32 * (shape.n_layers * (n_cu + 1)))()
+    _check(lib().mk_plan_streams(ctypes.byref(cfg), int(batch), int(n_cu), tasks, n.value, offs, amap,
+                                 ctypes.byref(n)), "mk_plan_streams")
+    names = [f for f, _ in TaskInfo._fields_]
+    streams = [[{k: getattr(tasks[i], k) for k in names} for i in range(offs[c], offs[c + 1])] for c in range(n_cu)]
+    L = shape.n_layers
+    return streams, [list(amap[l * (n_cu + 1):(l + 1) * (n_cu + 1)]) for l in range(L)]
 
 
 def _stream_handle(stream):

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <new>
@@ -142,6 +143,19 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
   p.skip_prev = env_int("MK_PLAN_SKIP_PREV", 2);
   p.attn_idle = env_int("MK_ATTN_IDLE", 1);
   p.ksplit = env_int("MK_KSPLIT", 1);
+  p.window_chunks = env_int("MK_WINDOW_COST", 6);
+  // MK_GEMV_STAGE_MODES="qkv:2,o:3,...": the tiling of single stages (1 row-owner,
+  // 2 stream-K, 3 stream-K with one-tile groups)
+  if (const char* v = getenv("MK_GEMV_STAGE_MODES")) {
+    const char* names[6] = {"qkv", "", "o", "gu", "down", "lm"};
+    for (int st = 0; st < 6; ++st) {
+      if (!names[st][0]) continue;
+      char key[8];
+      snprintf(key, sizeof key, "%s:", names[st]);
+      const char* f = strstr(v, key);
+      if (f && (f == v || f[-1] == ',')) p.stage_mode[st] = atoi(f + strlen(key));
+    }
+  }
   p.ksplit_min_windows = env_int("MK_KSPLIT_MIN_WINDOWS", 5);
   return p;
 }
@@ -228,6 +242,45 @@ int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats*
     }
     out->attn_slots_valid = valid;
   }
+  free_plan(&P);
+  return MK_OK;
+}
+
+int mk_plan_streams(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_task_info* tasks, int32_t cap,
+                    int32_t* cu_offsets, int32_t* attn_map, int32_t* n_tasks) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!n_tasks || !cu_offsets || n_cu < 1 || batch < 1 || batch > cfg->max_batch || cap < 0)
+    return MK_ERR_INVALID_ARG;
+  const int mfma_min = std::min(8, std::max(1, env_int("MK_MFMA_MIN_BATCH", 8)));
+  PlanCfg pc = plan_cfg(cfg, n_cu, xb_for(163840, nslot_for(163840, batch, mfma_min)), mfma_min);
+  Plan P;
+  rc = build_plan(pc, batch, &P);
+  if (rc) return rc;
+  *n_tasks = P.n_tasks;
+  if (P.n_tasks > cap || !tasks) {
+    free_plan(&P);
+    return MK_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < P.n_tasks; ++i) {
+    const Task& t = P.tasks[i];
+    mk_task_info& o = tasks[i];
+    o.type = t.type;
+    o.stage = t.stage;
+    o.layer = t.layer;
+    o.row0 = t.row0;
+    o.nsub = t.nsub;
+    o.k0 = t.k0;
+    o.k1 = t.k1;
+    o.ks = t.ks;
+    o.nks = t.nks;
+    o.group = t.group;
+    o.part_slot = t.part_slot;
+    o.nchunks = t.nchunks;
+    o.flags = t.flags;
+  }
+  for (int c = 0; c <= n_cu; ++c) cu_offsets[c] = P.task_off[c];
+  if (attn_map) memcpy(attn_map, P.attn_map, sizeof(int) * (size_t)cfg->n_layers * (n_cu + 1));
   free_plan(&P);
   return MK_OK;
 }

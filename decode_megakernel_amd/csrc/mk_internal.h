@@ -188,6 +188,8 @@ struct PlanCfg {
   int xb_bytes;         // LDS bytes available to stage a GEMV input slice
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
   int gemv_mode = 0;    // 0: cheaper of row-owner / stream-K per stage, 1: row-owner, 2: stream-K
+  double window_chunks = 6.0;  // planner cost of staging one LDS input window, in streamed chunks
+  int stage_mode[6] = {0, 0, 0, 0, 0, 0};  // per stage, overrides gemv_mode when non-zero; 3: stream-K, one-tile groups
   int attn_idle = 1;    // attention prefers the CUs its layer's QKV stage left idle
   int ksplit = 1;       // K-split stages whose tasks would need many LDS input windows
   int ksplit_min_windows = 5;  // ... at least this many (per task of the tiling it replaces)

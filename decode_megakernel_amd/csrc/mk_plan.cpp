@@ -57,10 +57,12 @@ int stage_k(const PlanCfg& p, int st) {
 // 16 KB weight chunk on the busiest CU: a split is charged kSplitChunks of
 // extra latency; staging the activation slice a task reads (b x K range,
 // 4 bytes per element in LDS) is charged per byte and per LDS window (each
-// window is a barrier plus a memory round trip while the ring sits full).
+// window is a barrier plus a memory round trip while the ring sits full;
+// PlanCfg::window_chunks, 6 by default: on Llama-3.2-1B at batch 8 and
+// Llama-3-8B at batch 1 a charge of 4 kept row-owner QKV / gate-up tilings
+// that measured 5% and 3% slower per step than the stream-K ones 6 picks).
 constexpr int kSplitChunks = 6;
 constexpr double kStageChunksPerChunk = 0.5;  // staged activation bytes, per 16 KB
-constexpr double kWindowChunks = 4.0;         // per staged window
 
 struct Tiling {
   bool owner = false;
@@ -74,20 +76,22 @@ struct Tiling {
   long long ncols = 1;
 };
 
-Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw, int b) {
+Tiling tile_stage(const PlanCfg& p, int st, int M, int K, int tpw, int b) {
+  const int mode = p.stage_mode[st] ? p.stage_mode[st] : p.gemv_mode;
   const int nst = (M + 15) / 16, nkb = (K + kKBlock - 1) / kKBlock;
   // K blocks of one LDS staging window at this batch (the kernel's rule)
   const int wkb = std::max(1, ((p.xb_bytes / (4 * b)) - 8) / kKBlock);
   // staging cost of one task over `kbs` K blocks
   auto stage_cost = [&](long long kbs) {
     const long long windows = (kbs + wkb - 1) / wkb;
-    return (double)b * (double)kbs * kKBlock * 4.0 / kChunkBytes * kStageChunksPerChunk + (double)windows * kWindowChunks;
+    return (double)b * (double)kbs * kKBlock * 4.0 / kChunkBytes * kStageChunksPerChunk + (double)windows * p.window_chunks;
   };
   Tiling best;
   best.nst = nst;
   best.nkb = nkb;
   double best_cost = 1e300;
   for (int gs = kGroupSub; gs >= 1; gs >>= 1) {
+    if (mode == 3 && gs != 1) continue;
     Tiling t = best;
     t.gs = gs;
     t.ngroups = (nst + gs - 1) / gs;
@@ -112,7 +116,7 @@ Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw, int b) {
   // previous task; otherwise every task stages all its windows again
   const double own_stage = stage_cost(nkb) * (double)(nkb <= wkb ? 1 : tasks_cu);
   const double own_cost = (double)tiles_cu * nkb + 0.25 * (double)tasks_cu + own_stage;
-  const bool use_owner = p.gemv_mode == 1 || (p.gemv_mode == 0 && own_cost <= best_cost);
+  const bool use_owner = mode == 1 || (mode == 0 && own_cost <= best_cost);
   // K-split: when a task's K range needs more than one staging window, cut K
   // into S pieces of at most one window each and deal (piece, sub-tile) units
   // K-major over the CUs, so each CU stages one input slice and streams its
@@ -126,7 +130,7 @@ Tiling tile_stage(const PlanCfg& p, int M, int K, int tpw, int b) {
   const Tiling& rep = use_owner ? own : best;
   const long long rep_kbs = rep.owner ? nkb : std::min<long long>(nkb, (rep.ncols + p.ncu - 1) / p.ncu);
   const long long rep_windows = (rep_kbs + wkb - 1) / wkb;
-  if (p.ksplit && p.gemv_mode == 0 && nkb > wkb && rep_windows >= p.ksplit_min_windows) {
+  if (p.ksplit && mode == 0 && nkb > wkb && rep_windows >= p.ksplit_min_windows) {
     Tiling k = own;
     k.owner = false;
     k.ks = true;
@@ -204,7 +208,7 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
   const int tpw = tiles_per_wave(mfma ? 0 : batch);
   for (int si = 0; si < 5; ++si) {
     int st = gemv_stages[si];
-    tl[st] = tile_stage(pc, stage_rows(pc, st), stage_k(pc, st), tpw, batch);
+    tl[st] = tile_stage(pc, st, stage_rows(pc, st), stage_k(pc, st), tpw, batch);
     const Tiling& T = tl[st];
     P.stage_owner[st] = T.owner ? 1 : 0;
     if (T.ks) {

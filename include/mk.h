@@ -320,6 +320,35 @@ typedef struct {
 
 int mk_plan(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_plan_stats* out);
 
+/* One instruction of a CU's stream, as the kernel reads it. */
+typedef struct {
+  int32_t type;       /* 1 embedding gather, 2 GEMV tile, 3 attention, 4 K-split finish */
+  int32_t stage;      /* 0 QKV, 1 attention, 2 O, 3 gate/up, 4 down, 5 LM head, 6 embedding */
+  int32_t layer;
+  int32_t row0;       /* GEMV / finish: first output row of the stage; embedding: first column */
+  int32_t nsub;       /* GEMV / finish: 16-row sub-tiles; embedding: columns */
+  int32_t k0, k1;     /* GEMV: K range */
+  int32_t ks, nks;    /* GEMV: piece index and pieces of a split K range */
+  int32_t group;      /* stream-K GEMV: row group */
+  int32_t part_slot;  /* split K: first partial slot of the group (stream-K, 1024 floats) or of the
+                         stage (K-split, 256-float tiles: sub-tile u's piece k at part_slot + u*nks + k) */
+  int32_t nchunks;    /* weight chunks the CU's loader streams for the task */
+  int32_t flags;      /* 1: the CU's last LM-head task (counts for the greedy tokens);
+                         2: K-split piece (publishes partial tiles) */
+} mk_task_info;
+
+/* Schedule export, host only: the per-CU instruction streams mk_create builds
+ * for `batch` on `n_cu` compute units, for inspection and for interpreting
+ * the schedule on the CPU (the AutoMegaKernel page's validator proves a
+ * schedule deadlock-free and race-free before it runs).  Writes the tasks of
+ * CU c at tasks[cu_offsets[c] .. cu_offsets[c+1]) (cu_offsets has n_cu + 1
+ * entries) and, when attn_map is not NULL, each layer's attention slots
+ * [n_layers][n_cu + 1] (slot of every CU, then the slot cap, 0 = none).
+ * *n_tasks receives the task count; MK_ERR_INVALID_ARG when it exceeds
+ * `cap` (nothing else written). */
+int mk_plan_streams(const mk_model_cfg* cfg, int32_t batch, int32_t n_cu, mk_task_info* tasks, int32_t cap,
+                    int32_t* cu_offsets, int32_t* attn_map, int32_t* n_tasks);
+
 #ifdef __cplusplus
 }
 #endif
