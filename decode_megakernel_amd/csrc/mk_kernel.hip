@@ -1058,6 +1058,10 @@ __device__ __forceinline__ bool rms_scales(DArgs A, Ctrl* c, const float* ss, in
 //      rows padded to kk1-kk0+8 elements, and the RMS scales of stages that
 //      normalize their input.  Skipped when the same slice is already staged.
 //      The input words are polled until they carry the step tag.
+#ifndef MK_STAGE_BATCH_MFMA
+#define MK_STAGE_BATCH_MFMA 4
+#endif
+template <int kStageBatch>
 __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int kk1, char* xb, Ctrl* c, CState& s, int w,
                             int lane, bool want_rms = true) {
   if (s.x_stage == t.stage && s.x_layer == t.layer && s.x_k0 == kk0 && s.x_k1 == kk1) return true;
@@ -1099,7 +1103,6 @@ __device__ __forceinline__ bool stage_input(DArgs A, const Task& t, int kk0, int
   // up to kStageBatch units per thread in flight at once: one memory round
   // trip per batch rather than per unit; the batch is loaded again until
   // every word carries its sequence's tag
-  constexpr int kStageBatch = 4;
   for (int u0 = tid; u0 < units; u0 += kStageBatch * kComputeThreads) {
     u32x4 va[kStageBatch], vb[kStageBatch];
     Spin sp = spin_start();
@@ -1457,7 +1460,7 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
     const int we = min(nkb, wb + wkb);
     const int kk0 = t.k0 + wb * kKBlock, kk1 = min(t.k1, t.k0 + we * kKBlock);
     const uint64_t ts0 = A->trace ? now_ticks() : 0;
-    if (!stage_input(A, t, kk0, kk1, xb, c, s, w, lane, !publish)) return false;
+    if (!stage_input<NB == 0 ? MK_STAGE_BATCH_MFMA : 4>(A, t, kk0, kk1, xb, c, s, w, lane, !publish)) return false;
     if (A->trace) s.t_stage += now_ticks() - ts0;
     gmark(0);
     const int ksp = kk1 - kk0 + 8, klen = kk1 - kk0, xlo_off = A->b * ksp * 2;
@@ -1655,10 +1658,16 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
         co_store_tag(pl, (uint32_t)(((size_t)t.ks * 1024 + ((lane >> 4) + 4 * j) * 16 + row) * 4), val[j], 1u);
     }
     if (own && t.ks == 0) {
-      constexpr int kSumBatch = 4;
-      const bool gu_up = t.stage == ST_GU && row < 8;
+      // every piece's partial in flight at once (up to kSumBatch pieces per
+      // round); for gate/up, lane ^ 8 holds the up row of a gate row and
+      // hands it over by a DPP move
+      constexpr int kSumBatch = 8;
+      const bool gu = t.stage == ST_GU;
+      // analysis builds: piece-0 wait for the other pieces (DOWN: stats word 30, others 31)
+      uint64_t* psp = (MK_PHASE_TRACE && A->trace && w == 0 && lane == 0) ? MK_PSTAT(c, t.stage == ST_DOWN ? 30 : 31) : nullptr;
+      const uint64_t tp0 = psp ? now_ticks() : 0;
       for (int k0 = 1; k0 < t.nks; k0 += kSumBatch) {
-        uint32_t pv[kSumBatch][4], pu[kSumBatch][4];
+        uint32_t pv[kSumBatch][4];
         Spin sp = spin_start();
         for (;;) {
 #pragma unroll
@@ -1666,15 +1675,13 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const uint32_t e = (uint32_t)((k0 + u) * 1024 + ((lane >> 4) + 4 * j) * 16 + row);
-              const bool ok = k0 + u < t.nks;
-              pv[u][j] = ok ? co_load4(pl, e * 4) : 1u;
-              pu[u][j] = ok && gu_up ? co_load4(pl, (e + 8) * 4) : 1u;
+              pv[u][j] = k0 + u < t.nks ? co_load4(pl, e * 4) : 1u;
             }
           uint32_t flags = 1u;
 #pragma unroll
           for (int u = 0; u < kSumBatch; ++u)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) flags &= pv[u][j] & pu[u][j];
+            for (int j = 0; j < 4; ++j) flags &= pv[u][j];
           if (__all((flags & 1u) != 0)) break;
           if (!poll_ok(A, c, sp)) return false;
         }
@@ -1684,11 +1691,13 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             co_store4(pl, (uint32_t)(((size_t)(k0 + u) * 1024 + ((lane >> 4) + 4 * j) * 16 + row) * 4), 0u);
-            val[j] += __uint_as_float(untag(pv[u][j]));
-            up[j] += gu_up ? __uint_as_float(untag(pu[u][j])) : 0.f;
+            const float pf = __uint_as_float(untag(pv[u][j]));
+            val[j] += pf;
+            if (gu) up[j] += dpp_f<kDppRor8>(pf);  // wave-uniform: every lane runs the move
           }
         }
       }
+      if (psp) trace_add(psp, now_ticks() - tp0);
       const int lr0 = tile_row0(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) gemv_epilogue(epi, c, lr0 + row, row, (lane >> 4) + 4 * j, val[j], up[j], resid[0][j], nwv[0], rmsv[j]);
@@ -1789,7 +1798,10 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
 //      order (a fixed order, so results do not depend on timing), clear the
 //      slots (their only reader; the next write is a step later) and run the
 //      stage's epilogue on the sums.  Compute wave w takes sub-tiles w, w+4, ...
-constexpr int kFinBatch = 8;  // pieces polled per batch, every load in flight
+#ifndef MK_FIN_BATCH
+#define MK_FIN_BATCH 16
+#endif
+constexpr int kFinBatch = MK_FIN_BATCH;  // pieces polled per batch, every load in flight
 __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
   Ctrl* c = ctrl_block(A);
@@ -1829,13 +1841,14 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
   for (int k = w; k < t.nsub; k += kComputeWaves) {
     const int u = t.row0 / 16 + k;
     const int lr = 16 * u + row;
-    // the piece values of this lane (rows lane & 15) and, for gate/up, of
-    // lane ^ 8 (a gate row's up row is 8 rows further in the tile); the
-    // residuals of O / down in flight with the first batch
+    // the piece values of this lane (rows lane & 15); for gate/up, lane ^ 8
+    // holds the up row of a gate row (8 rows further in the tile) and hands
+    // it over by a DPP move after the loads; the residuals of O / down in
+    // flight with the first batch
     const uint32_t slot0 = (uint32_t)t.part_slot + (uint32_t)u * nks;
     float val[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f}, rs[4] = {0.f, 0.f, 0.f, 0.f};
     for (int p0 = 0; p0 < nks; p0 += kFinBatch) {
-      u32x4 pv[kFinBatch], pu[kFinBatch];
+      u32x4 pv[kFinBatch];
       Spin sp = spin_start();
       for (;;) {
 #pragma unroll
@@ -1843,7 +1856,6 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
           const bool ok = p0 + q < nks;
           const uint32_t base = (slot0 + (uint32_t)(p0 + q)) * 1024u;
           pv[q] = ok ? co_load16(pbase, base + 16u * lane) : u32x4{1u, 1u, 1u, 1u};
-          pu[q] = (ok && gu) ? co_load16(pbase, base + 16u * (lane ^ 8)) : u32x4{1u, 1u, 1u, 1u};
         }
         bool rok = true;
         if (has_resid && p0 == 0) {
@@ -1857,8 +1869,7 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
         }
         uint32_t flags = 1u;
 #pragma unroll
-        for (int q = 0; q < kFinBatch; ++q)
-          flags &= pv[q].x & pv[q].y & pv[q].z & pv[q].w & pu[q].x & pu[q].y & pu[q].z & pu[q].w;
+        for (int q = 0; q < kFinBatch; ++q) flags &= pv[q].x & pv[q].y & pv[q].z & pv[q].w;
         if (__all(rok && (flags & 1u) != 0)) break;
         if (!poll_ok(A, c, sp)) return false;
       }
@@ -1866,15 +1877,17 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
       for (int q = 0; q < kFinBatch; ++q) {
         if (p0 + q >= nks) break;
         co_store16(pbase, (slot0 + (uint32_t)(p0 + q)) * 1024u + 16u * lane, u32x4{0u, 0u, 0u, 0u});
-        const u32x4 a = untag4(pv[q]), b = untag4(pu[q]);
+        const u32x4 a = untag4(pv[q]);
         val[0] += __uint_as_float(a.x);
         val[1] += __uint_as_float(a.y);
         val[2] += __uint_as_float(a.z);
         val[3] += __uint_as_float(a.w);
-        up[0] += __uint_as_float(b.x);
-        up[1] += __uint_as_float(b.y);
-        up[2] += __uint_as_float(b.z);
-        up[3] += __uint_as_float(b.w);
+        if (gu) {  // wave-uniform: every lane runs the moves
+          up[0] += dpp_f<kDppRor8>(__uint_as_float(a.x));
+          up[1] += dpp_f<kDppRor8>(__uint_as_float(a.y));
+          up[2] += dpp_f<kDppRor8>(__uint_as_float(a.z));
+          up[3] += dpp_f<kDppRor8>(__uint_as_float(a.w));
+        }
       }
     }
 #pragma unroll
@@ -2799,7 +2812,15 @@ __global__ __launch_bounds__(kThreads, 1) void mk_step_kernel(DevArgs args) {
   (void)args;
   DArgs A = (DArgs)__builtin_amdgcn_kernarg_segment_ptr();
   Ctrl* c = ctrl_block(A);
-  const int cu = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+#ifndef MK_XCD_MAP
+#define MK_XCD_MAP 0
+#endif
+  // MK_XCD_MAP: work-groups are dealt round-robin over the 8 XCDs, so plan
+  // CU p = (block % 8) * (grid / 8) + block / 8 puts consecutive plan CUs on
+  // one XCD (and its L2)
+  const int cu = (MK_XCD_MAP && gridDim.x % 8 == 0) ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                                    : (int)blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 
   // zero this CU's slice of the bank the next step will use
   {
