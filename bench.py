@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--per-config-steps", type=int, default=10)
     ap.add_argument("--no-per-op", action="store_true",
                     help="skip the per-operation baseline beside the per-config workloads")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="run every workload on a paged KV cache of BLOCK-position blocks (blocks of each "
+                         "sequence scattered over the pool; no CPU or per-operation baselines)")
+    ap.add_argument("--paged-order", choices=("permuted", "sequential"), default="permuted",
+                    help="block ids of the paged pools: a seeded permutation, or each sequence's blocks in order")
     ap.add_argument("--context-sweep", action="store_true",
                     help="Qwen3-8B-shaped model at batch 1 and 8 over contexts 64-4096, with and without "
                          "context routing (mk_set_context_bound); prints one JSON line and exits")
@@ -81,16 +86,25 @@ class Run:
     the start) and engine on the GPU; phases run back to back on the same
     engine and cache, so a sequence that joins finds the others mid-run."""
 
-    def __init__(self, wl, steps_per_phase):
+    def __init__(self, wl, steps_per_phase, paged=0, paged_order="permuted"):
         import torch
-        from mkinputs import make_weights, make_kv_cache, draw_contexts, draw_tokens, kv_capacity
+        from mkinputs import make_weights, make_kv_cache, make_paged_kv, draw_contexts, draw_tokens, kv_capacity
         from decode_megakernel_amd.binding import DecodeEngine
         self.wl, self.shape = wl, wl.shape
         self.ctx = draw_contexts(wl.seed, wl.batch_cap, wl.ctx_lo, wl.ctx_hi)
         total = steps_per_phase * len(wl.phases)
         self.seq_cap = kv_capacity(max(self.ctx) + 1, total)
         self.weights = make_weights(self.shape, wl.seed, device="cuda")
-        self.K, self.V = make_kv_cache(self.shape, wl.seed, self.ctx, wl.batch_cap, self.seq_cap, device="cuda")
+        # paged: the same rows in pools of `paged`-position blocks, each
+        # sequence's blocks scattered over the pool by a seeded permutation
+        self.paged = paged
+        if paged:
+            self.K = self.V = None
+            self.Kp, self.Vp, self.btab = make_paged_kv(self.shape, wl.seed, self.ctx, wl.batch_cap, self.seq_cap,
+                                                        paged, device="cuda", permute=paged_order == "permuted")
+        else:
+            self.K, self.V = make_kv_cache(self.shape, wl.seed, self.ctx, wl.batch_cap, self.seq_cap,
+                                           device="cuda")
         self.first_tok = torch.tensor(draw_tokens(wl.seed, wl.batch_cap, self.shape.vocab), dtype=torch.int32,
                                       device="cuda")
         self.tok = torch.zeros((2, wl.batch_cap), dtype=torch.int32, device="cuda")
@@ -121,8 +135,12 @@ class Run:
 
         def step(k):
             s = s0 + k
-            self.eng.step(self.tok[s % 2, :b], pos[k], lens[k], self.K, self.V, self.logits[:b],
-                          self.tok[(s + 1) % 2, :b], stream=stream, batch=b)
+            if self.paged:
+                self.eng.step_paged(self.tok[s % 2, :b], pos[k], lens[k], self.Kp, self.Vp, self.btab,
+                                    self.logits[:b], self.tok[(s + 1) % 2, :b], stream=stream, batch=b)
+            else:
+                self.eng.step(self.tok[s % 2, :b], pos[k], lens[k], self.K, self.V, self.logits[:b],
+                              self.tok[(s + 1) % 2, :b], stream=stream, batch=b)
 
         for k in range(warmup):
             step(k)
@@ -157,6 +175,8 @@ class Run:
         import torch
         self.eng.close()
         del self.weights, self.K, self.V
+        if self.paged:
+            del self.Kp, self.Vp, self.btab
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
@@ -413,7 +433,9 @@ def main():
     n = args.warmup + args.steps
     # the headline: the workload's last phase after its earlier ones (a batch
     # that grows runs its first phase untimed, warmup only)
-    run = Run(wl, n)
+    if args.paged:
+        args.no_cpu_baseline = args.no_per_op = True
+    run = Run(wl, n, args.paged, args.paged_order)
     for p in wl.phases[:-1]:
         run.phase(p.batch, args.warmup, 1)
     ph = run.phase(wl.phases[-1].batch, args.warmup, args.steps)
@@ -432,7 +454,7 @@ def main():
             if key == wl.key:
                 continue
             w2 = WORKLOADS[key]
-            r2 = Run(w2, args.warmup + k)
+            r2 = Run(w2, args.warmup + k, args.paged, args.paged_order)
             rec = {"note": w2.note, "phases": []}
             for p in w2.phases:
                 rec["phases"].append(summarize(r2.phase(p.batch, args.warmup, k)))
@@ -460,6 +482,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded random-init bf16 weights N(0,0.02), N(0,1) prompt KV, uniform first tokens",
         "config": {"workload": wl.key, "shape": wl.shape.name, "batch": b,
+                   "kv_cache": f"paged, {args.paged}-position blocks, {args.paged_order}" if args.paged else "contiguous",
                    "context_at_first_timed_step": ph["context_at_first_timed_step"], "note": wl.note},
         "mbu": round(achieved / HBM_PEAK_BYTES_PER_S, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK_BYTES_PER_S / 1e9,

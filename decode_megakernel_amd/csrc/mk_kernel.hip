@@ -852,11 +852,12 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
           const int rows = min(rpc, P.ncached - ch * rpc);
           char* dst = ring + (size_t)R.slot * kSlotBytes;
           const size_t r0 = kv_row<true>(A, t.layer, P.i, P.g, p0) * A->hd;
-          if (A->btab) {
-            // a chunk (at most 64 rows, blocks at least 64 positions) spans at most two blocks
-            const int lb = p0 / A->bsize;
-            const int split = min(rows, (lb + 1) * A->bsize - p0);
-            const size_t r1 = split < rows ? kv_row<true>(A, t.layer, P.i, P.g, (lb + 1) * A->bsize) * A->hd : r0;
+          // a paged chunk (at most 64 rows, blocks at least 64 positions)
+          // spans at most two blocks, rows [0, split) in the first; one that
+          // lies in a single block loads like a contiguous chunk
+          const int split = A->btab ? min(rows, (p0 / A->bsize + 1) * A->bsize - p0) : rows;
+          if (split < rows) {
+            const size_t r1 = kv_row<true>(A, t.layer, P.i, P.g, p0 + split) * A->hd;
             if (A->hd == 128)
               dma_attn_chunk<128, true>(A, A->kc + r0, A->vc + r0, A->kc + r1, A->vc + r1, split, rows, lane, dst, A->G == 1);
             else

@@ -148,6 +148,34 @@ def make_kv_cache(shape: ModelShape, seed: int, contexts, batch_cap: int, seq_ca
     return K, V
 
 
+def make_paged_kv(shape: ModelShape, seed: int, contexts, batch_cap: int, seq_cap: int, block: int,
+                  device="cpu", permute: bool = True):
+    """The rows of make_kv_cache in paged pools: K, V bf16
+    [L][n_blocks][n_kv][block][head_dim] with n_blocks = batch_cap * seq_cap /
+    block, and the int32 block table [batch_cap][seq_cap / block] (entry j of
+    row i: the pool block holding positions j*block .. of sequence i).  Block
+    ids are a seeded permutation (a sequence's blocks scattered over the
+    pool), or in order when `permute` is false."""
+    if seq_cap % block:
+        raise ValueError(f"block {block} must divide the capacity {seq_cap}")
+    L, nkv, hd = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    nb = seq_cap // block
+    n_blocks = batch_cap * nb
+    g = _generator(seed, "kv.block_table", "cpu")
+    perm = torch.randperm(n_blocks, generator=g) if permute else torch.arange(n_blocks)
+    table = perm.view(batch_cap, nb).to(torch.int32).to(device)
+    dst = perm.to(device)
+    Kp = torch.empty((L, n_blocks, nkv, block, hd), dtype=torch.bfloat16, device=device)
+    Vp = torch.empty_like(Kp)
+    for l in range(L):
+        k, v = make_kv_layer(shape, seed, contexts, batch_cap, seq_cap, l, device)
+        for src, pool in ((k, Kp), (v, Vp)):
+            blocks = src.view(batch_cap, nkv, nb, block, hd).permute(0, 2, 1, 3, 4).reshape(n_blocks, nkv, block, hd)
+            pool[l].index_copy_(0, dst, blocks)
+        del k, v
+    return Kp, Vp, table
+
+
 def bf16_bits(t: torch.Tensor):
     """Host numpy uint16 view of a bf16 tensor's bits (copies off the device)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")

@@ -88,3 +88,25 @@ def test_plan_small_shapes_all_batches(shape):
 def test_plan_rejects_batch_over_capacity():
     with pytest.raises(binding.MKError):
         binding.plan(TINY_LLAMA, 5, 256, max_batch=4)
+
+
+@pytest.mark.parametrize("permute", [True, False])
+def test_paged_pools_hold_the_contiguous_rows(permute):
+    """The benchmark's paged pools: block table entry j of row i names the
+    pool block that holds positions j*block .. of sequence i, bit for bit the
+    rows of the contiguous cache; the block ids are a permutation."""
+    import torch
+    from mkinputs import make_kv_cache, make_paged_kv
+    from mkinputs.configs import SMALL_MHA_H64 as sh
+    ctx, B, S, bs = [100, 300, 5], 3, 512, 128
+    K, V = make_kv_cache(sh, 7, ctx, B, S)
+    Kp, Vp, bt = make_paged_kv(sh, 7, ctx, B, S, bs, permute=permute)
+    assert sorted(bt.flatten().tolist()) == list(range(B * S // bs))
+    if not permute:
+        assert bt.flatten().tolist() == list(range(B * S // bs))
+    for l in range(sh.n_layers):
+        for i in range(B):
+            for j in range(S // bs):
+                blk = int(bt[i, j])
+                assert torch.equal(Kp[l, blk].view(torch.int16), K[l, i, :, j * bs:(j + 1) * bs].view(torch.int16))
+                assert torch.equal(Vp[l, blk].view(torch.int16), V[l, i, :, j * bs:(j + 1) * bs].view(torch.int16))
