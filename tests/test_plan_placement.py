@@ -65,3 +65,29 @@ def test_attention_slots_are_permutations(shape, batch, ncu):
     # a cap, when set, is the number of CUs QKV left idle
     if st["attn_slot_cap"]:
         assert st["attn_slot_cap"] == ncu - st["stage_cus"][QKV]
+
+
+def _stage_balance(shape, batch):
+    """Per GEMV stage (layer 0, and the LM head): mean / max weight bytes per
+    CU over the 256 CUs, from the exported task streams."""
+    streams, _ = binding.plan_streams(shape, batch, 256)
+    per = {}
+    for c, tasks in enumerate(streams):
+        for t in tasks:
+            if t["type"] == 2 and (t["layer"] == 0 or t["stage"] == LM):
+                per.setdefault(t["stage"], [0] * 256)[c] += 16 * t["nsub"] * (t["k1"] - t["k0"]) * 2
+    return {st: sum(v) / len(v) / max(v) for st, v in per.items()}
+
+
+@pytest.mark.parametrize("key,batch", [("llama3.2-1b-b8", 8), ("llama3-8b-b1", 1), ("llama3-8b-b8to9", 8),
+                                       ("llama3-8b-b8to9", 9), ("llama2-13b-b16", 16)])
+def test_large_stages_are_balanced(key, batch):
+    """Gate/up, down and the LM head (the stages that carry most weight
+    bytes) put within 3% of the mean number of bytes on the busiest CU.  QKV
+    and O may be coarser: their finer tilings measured slower (one-tile
+    stream-K groups, row-owner, stream-K instead of K-split)."""
+    from mkinputs import WORKLOADS
+    bal = _stage_balance(WORKLOADS[key].shape, batch)
+    for st in (GU, DOWN, LM):
+        assert bal[st] >= 0.97, (key, batch, st, bal)
+    assert min(bal.values()) >= 0.74, bal
