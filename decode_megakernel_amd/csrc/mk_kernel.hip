@@ -191,6 +191,15 @@ __device__ __forceinline__ void split8(u32x4 a, u32x4 b, u32x4& hi, u32x4& lo) {
 
 // LDS accessors
 __device__ __forceinline__ u32x4 lds_ld16(const char* p) { return *(const u32x4*)p; }
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): every lane loads 4
+// 16-bit elements at its address; within each block of 16 lanes, lane 4a + c
+// receives element c of the loads of lanes a, a + 4, a + 8 and a + 12, in that
+// order (the 4 x 4 element transpose of a lane quad's 64-bit loads)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_ld8_tr16(const char* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(char*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
 __device__ __forceinline__ void lds_st16(char* p, u32x4 v) { *(u32x4*)p = v; }
 
 // ------------------------------------------------------------ CU control
@@ -2553,8 +2562,11 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
           for (int i = 0; i < 4; ++i) O[nb][i] *= fl[i];
       }
       // P.V on MFMA: A = P^T rows (heads) x 32 cached rows, B = 32 V rows x
-      // 16 dims gathered from the row-major chunk
-      const uint16_t* vrow = (const uint16_t*)(slot + 8192);
+      // 16 dims of the row-major chunk, read transposed: lane s of each
+      // 16-lane block loads dims 4 (s & 3) .. + 3 of row (s >> 2), so lane
+      // r16 of block lr receives dim r16 of 4 consecutive rows; two reads
+      // give rows r0 .. r0 + 7
+      const char* vrow = slot + 8192 + (size_t)(((lane & 15) >> 2) * HD + 4 * (lane & 3)) * 2;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int r0 = ks * 32 + 8 * lr;
@@ -2562,12 +2574,9 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         const u32x4 al = lds_ld16((const char*)(pt_lo + hsel * RPC + r0));
 #pragma unroll
         for (int nb = 0; nb < NB16; ++nb) {
-          const uint16_t* vp = vrow + r0 * HD + nb * 16 + r16;
-          u32x4 bv;
-          bv.x = (uint32_t)vp[0] | ((uint32_t)vp[HD] << 16);
-          bv.y = (uint32_t)vp[2 * HD] | ((uint32_t)vp[3 * HD] << 16);
-          bv.z = (uint32_t)vp[4 * HD] | ((uint32_t)vp[5 * HD] << 16);
-          bv.w = (uint32_t)vp[6 * HD] | ((uint32_t)vp[7 * HD] << 16);
+          const char* vp = vrow + (size_t)(r0 * HD + nb * 16) * 2;
+          const u32x2 v03 = lds_ld8_tr16(vp), v47 = lds_ld8_tr16(vp + 4 * HD * 2);
+          const u32x4 bv = {v03.x, v03.y, v47.x, v47.y};
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al), __builtin_bit_cast(bf16x8_t, bv),
                                                           O[nb], 0, 0, 0);
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bv),
