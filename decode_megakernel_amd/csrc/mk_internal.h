@@ -43,7 +43,8 @@ constexpr int kRedBytes = 4 * 256 * 4;
 // over head_dim 64 / group 8 and head_dim 128 / group 4
 constexpr int kAttnBatch = 4;
 constexpr int attn_lds_floats(int hd, int gm) {
-  return 2 * 4 * gm * (hd + 4) + kAttnBatch * gm * hd + kAttnBatch * 2 * hd + 4 * (4096 / hd) * gm;  // per wave: P^T as bf16 hi + lo, [group][rows per chunk] each
+  // per wave: P as bf16 hi + lo, [rows per chunk][group padded to 4 or 8] each
+  return 2 * 4 * gm * (hd + 4) + kAttnBatch * gm * hd + kAttnBatch * 2 * hd + 4 * (4096 / hd) * (gm <= 4 ? 4 : 8);
 }
 constexpr int kAttnStateBytes =
     4 * (attn_lds_floats(64, 8) > attn_lds_floats(128, 4) ? attn_lds_floats(64, 8) : attn_lds_floats(128, 4));

@@ -2048,7 +2048,8 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
   const int stride_st = kComputeWaves * GM * SW;
   float* qs = stb + 2 * stride_st;
   float* knv = qs + kAttnBatch * GM * HD;
-  float* pb = knv + kAttnBatch * 2 * HD + w * RPC * GM;  // P^T: 2 planes x GM heads x RPC bf16
+  constexpr int GMP = GM <= 4 ? 4 : 8;  // heads per probability row (the group padded to 4 or 8)
+  float* pb = knv + kAttnBatch * 2 * HD + w * RPC * GMP;  // P: 2 planes x RPC rows x GMP heads, bf16
   const float* qkv_l = A->qkv + (size_t)l * A->bcap * A->nqkv;
   const uint32_t tags = A->rowtag;
   // the staging buffer is rewritten below (queries, new rows, wave states):
@@ -2477,9 +2478,13 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
     for (int nb = 0; nb < NB16; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the value of a per-head wave-uniform array for this lane's head 4 lr + i
     auto lane_head = [&](const float (&v)[GM], int i) { return (GM > 4 && lr == 1) ? v[(4 + i) % GM] : v[i % GM]; };
-    const int hsel = min(r16, GM - 1);  // A-operand rows past the group repeat its last head
-    uint16_t* pt_hi = (uint16_t*)pb;    // P^T [GM heads][RPC rows] as bf16 hi, then lo
-    uint16_t* pt_lo = pt_hi + GM * RPC;
+    uint16_t* p_hi = (uint16_t*)pb;  // P [RPC rows][GMP heads] as bf16 hi, then lo
+    uint16_t* p_lo = p_hi + RPC * GMP;
+    // A operand of P.V read transposed: lane s of each 16-lane block loads
+    // heads 4 min(s & 3, GMP / 4 - 1) .. + 3 of row s >> 2, so lane r16 <
+    // GMP receives head r16 of 4 consecutive rows (rows past GMP repeat
+    // heads; rows past the group are never stored)
+    const int p_off = ((lane & 15) >> 2) * GMP + 4 * min(lane & 3, GMP / 4 - 1);
     mark(0);
     // cached rows, streamed by the loader
     for (int ch = 0; ch < P.nch; ++ch) {
@@ -2523,30 +2528,36 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
         fa[h] = mnew[h] == -INFINITY ? 1.f : fast_exp2(mrun[h] - mnew[h]);
       }
       // probabilities of this lane's rows for its heads and their row sums;
-      // P^T to LDS as bf16 hi + lo planes (the A operand of P.V)
-      float ls[4];
+      // P to LDS as bf16 hi + lo planes, a row's 4 heads in one 8-byte store
+      // (the A operand of P.V)
+      float mh[4], sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mh = lane_head(mnew, i);
-        const int hh = 4 * lr + i;
-        float sum = 0.f;
+      for (int i = 0; i < 4; ++i) mh[i] = lane_head(mnew, i);
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
+        uint32_t ph[2] = {0u, 0u}, pl[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
           // masked rows hold -inf and give exp2(-inf) = 0; mh is finite
           // (every chunk has at least one row)
-          const float pv = fast_exp2(S[rb][i] - mh);
-          sum += pv;
-          if (hh < GM) {
-            // hi = p truncated to bf16, lo = the remainder truncated to bf16
-            // (p in [0, 1]: the pair keeps p to about 2^-16)
-            const uint32_t bits = __float_as_uint(pv);
-            const float rem = pv - __uint_as_float(bits & 0xFFFF0000u);
-            pt_hi[hh * RPC + rb * 16 + r16] = (uint16_t)(bits >> 16);
-            pt_lo[hh * RPC + rb * 16 + r16] = (uint16_t)(__float_as_uint(rem) >> 16);
-          }
+          const float pv = fast_exp2(S[rb][i] - mh[i]);
+          sum[i] += pv;
+          // hi = p truncated to bf16, lo = the remainder truncated to bf16
+          // (p in [0, 1]: the pair keeps p to about 2^-16)
+          const uint32_t bits = __float_as_uint(pv);
+          const float rem = pv - __uint_as_float(bits & 0xFFFF0000u);
+          ph[i >> 1] |= (bits >> 16) << (16 * (i & 1));
+          pl[i >> 1] |= (__float_as_uint(rem) >> 16) << (16 * (i & 1));
         }
-        ls[i] = group_sum<16>(sum);
+        if (4 * lr < GMP) {
+          const int e = (rb * 16 + r16) * GMP + 4 * lr;
+          *(u32x2*)(p_hi + e) = u32x2{ph[0], ph[1]};
+          *(u32x2*)(p_lo + e) = u32x2{pl[0], pl[1]};
+        }
       }
+      float ls[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ls[i] = group_sum<16>(sum[i]);
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         lrun[h] = lrun[h] * fa[h] + bcast(ls[h & 3], 16 * (h >> 2));
@@ -2570,8 +2581,10 @@ __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lan
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int r0 = ks * 32 + 8 * lr;
-        const u32x4 ah = lds_ld16((const char*)(pt_hi + hsel * RPC + r0));
-        const u32x4 al = lds_ld16((const char*)(pt_lo + hsel * RPC + r0));
+        const char* pa = (const char*)(p_hi + r0 * GMP + p_off);
+        const u32x2 h03 = lds_ld8_tr16(pa), h47 = lds_ld8_tr16(pa + 4 * GMP * 2);
+        const u32x2 l03 = lds_ld8_tr16(pa + RPC * GMP * 2), l47 = lds_ld8_tr16(pa + (RPC + 4) * GMP * 2);
+        const u32x4 ah = {h03.x, h03.y, h47.x, h47.y}, al = {l03.x, l03.y, l47.x, l47.y};
 #pragma unroll
         for (int nb = 0; nb < NB16; ++nb) {
           const char* vp = vrow + (size_t)(r0 * HD + nb * 16) * 2;
