@@ -144,6 +144,8 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
   p.attn_idle = env_int("MK_ATTN_IDLE", 1);
   p.ksplit = env_int("MK_KSPLIT", 1);
   p.window_chunks = env_int("MK_WINDOW_COST", 6);
+  p.split_chunks = env_int("MK_SPLIT_COST", 6);
+  p.ksplit_aligned = env_int("MK_KSPLIT_ALIGNED", 1);
   // MK_GEMV_STAGE_MODES="qkv:2,o:3,...": the tiling of single stages (1 row-owner,
   // 2 stream-K, 3 stream-K with one-tile groups)
   if (const char* v = getenv("MK_GEMV_STAGE_MODES")) {

@@ -190,6 +190,8 @@ struct PlanCfg {
   int mfma_min_batch;   // batch at or above which projections use MFMA tiles
   int gemv_mode = 0;    // 0: cheaper of row-owner / stream-K per stage, 1: row-owner, 2: stream-K
   double window_chunks = 6.0;  // planner cost of staging one LDS input window, in streamed chunks
+  double split_chunks = 6.0;   // planner cost of splitting a stream-K group over CUs, in streamed chunks
+  int ksplit_aligned = 1;      // K-split units dealt piece-aligned (each CU one input window)
   int stage_mode[6] = {0, 0, 0, 0, 0, 0};  // per stage, overrides gemv_mode when non-zero; 3: stream-K, one-tile groups
   int attn_idle = 1;    // attention prefers the CUs its layer's QKV stage left idle
   int ksplit = 1;       // K-split stages whose tasks would need many LDS input windows

@@ -54,14 +54,13 @@ int stage_k(const PlanCfg& p, int st) {
 //    row-group boundaries, and a row group whose K range is split over
 //    several CUs is finished by the last of its pieces.
 // The cheaper one is chosen per stage.  Costs are in units of one streamed
-// 16 KB weight chunk on the busiest CU: a split is charged kSplitChunks of
+// 16 KB weight chunk on the busiest CU: a split is charged PlanCfg::split_chunks of
 // extra latency; staging the activation slice a task reads (b x K range,
 // 4 bytes per element in LDS) is charged per byte and per LDS window (each
 // window is a barrier plus a memory round trip while the ring sits full;
 // PlanCfg::window_chunks, 6 by default: on Llama-3.2-1B at batch 8 and
 // Llama-3-8B at batch 1 a charge of 4 kept row-owner QKV / gate-up tilings
 // that measured 5% and 3% slower per step than the stream-K ones 6 picks).
-constexpr int kSplitChunks = 6;
 constexpr double kStageChunksPerChunk = 0.5;  // staged activation bytes, per 16 KB
 
 struct Tiling {
@@ -101,7 +100,7 @@ Tiling tile_stage(const PlanCfg& p, int st, int M, int K, int tpw, int b) {
     // a CU's columns touch at least one group: one staged slice per group touched
     const long long groups_cu = std::max(1LL, (per_cu + nkb - 1) / nkb);
     double cost = (double)per_cu * gs + 0.25 * (double)per_cu / nkb + (gs < kGroupSub ? 0.01 : 0.0) +
-                  (split ? kSplitChunks : 0) + stage_cost(std::min<long long>(per_cu, nkb)) * (double)groups_cu;
+                  (split ? p.split_chunks : 0) + stage_cost(std::min<long long>(per_cu, nkb)) * (double)groups_cu;
     if (cost < best_cost) {
       best_cost = cost;
       best = t;
@@ -283,12 +282,24 @@ int build_plan(const PlanCfg& pc, int batch, Plan* out) {
     const Tiling& T = tl[st];
     const int nst = (M + 15) / 16;
     if (T.ks) {
-      // units (piece s, sub-tile u), s-major, dealt evenly over the CUs; a
-      // CU's run of units with one s becomes tasks of at most tmax sub-tiles
+      // units (piece s, sub-tile u), s-major.  With at least as many CUs as
+      // pieces, piece s gets CUs [s ncu / S, (s+1) ncu / S) and its sub-tiles
+      // are split evenly over them, so no CU stages two input windows (a CU
+      // whose units straddled two pieces restaged and ran ~9 us behind the
+      // others at Llama-2-13B b16, for at most one unit more per CU this
+      // way); otherwise the units are dealt evenly over the CUs.  A CU's run
+      // of units with one s becomes tasks of at most tmax sub-tiles.
       const long long units = (long long)T.S * nst;
+      const bool aligned = ncu >= T.S && pc.ksplit_aligned;
       std::fill(prev_used.begin(), prev_used.end(), 1);
       for (int c = 0; c < ncu; ++c) {
-        const long long u0 = units * c / ncu, u1 = units * (c + 1) / ncu;
+        long long u0 = units * c / ncu, u1 = units * (c + 1) / ncu;
+        if (aligned) {
+          const int sp = (int)((long long)c * T.S / ncu);
+          const int ca = (int)(((long long)sp * ncu + T.S - 1) / T.S), cb = (int)(((long long)(sp + 1) * ncu + T.S - 1) / T.S);
+          u0 = (long long)sp * nst + (long long)nst * (c - ca) / (cb - ca);
+          u1 = (long long)sp * nst + (long long)nst * (c + 1 - ca) / (cb - ca);
+        }
         for (long long x = u0; x < u1;) {
           const int sp = (int)(x / nst), ua = (int)(x % nst);
           const int ub = (int)std::min<long long>(nst, ua + (u1 - x));

@@ -69,25 +69,36 @@ def test_attention_slots_are_permutations(shape, batch, ncu):
 
 def _stage_balance(shape, batch):
     """Per GEMV stage (layer 0, and the LM head): mean / max weight bytes per
-    CU over the 256 CUs, from the exported task streams."""
+    CU over the 256 CUs, and the most K windows one CU's K-split units span
+    (each distinct window is one more staging of the input), from the
+    exported task streams."""
     streams, _ = binding.plan_streams(shape, batch, 256)
-    per = {}
+    per, wins, ksplit = {}, {}, set()
     for c, tasks in enumerate(streams):
         for t in tasks:
             if t["type"] == 2 and (t["layer"] == 0 or t["stage"] == LM):
                 per.setdefault(t["stage"], [0] * 256)[c] += 16 * t["nsub"] * (t["k1"] - t["k0"]) * 2
-    return {st: sum(v) / len(v) / max(v) for st, v in per.items()}
+                if t["flags"] & 2:  # a K-split piece
+                    ksplit.add(t["stage"])
+                    wins.setdefault(t["stage"], [set() for _ in range(256)])[c].add(t["k0"])
+    bal = {st: sum(v) / len(v) / max(v) for st, v in per.items()}
+    return bal, {st: max(len(x) for x in v) for st, v in wins.items()}, ksplit
 
 
 @pytest.mark.parametrize("key,batch", [("llama3.2-1b-b8", 8), ("llama3-8b-b1", 1), ("llama3-8b-b8to9", 8),
                                        ("llama3-8b-b8to9", 9), ("llama2-13b-b16", 16)])
 def test_large_stages_are_balanced(key, batch):
     """Gate/up, down and the LM head (the stages that carry most weight
-    bytes) put within 3% of the mean number of bytes on the busiest CU.  QKV
-    and O may be coarser: their finer tilings measured slower (one-tile
+    bytes) put within 3% of the mean number of bytes on the busiest CU, or
+    within 7% for K-split stages, whose units are dealt piece by piece so
+    that every CU stages a single input window (a CU that straddled two
+    pieces restaged and ran ~9 us behind, more than the extra unit costs).
+    QKV and O may be coarser: their finer tilings measured slower (one-tile
     stream-K groups, row-owner, stream-K instead of K-split)."""
     from mkinputs import WORKLOADS
-    bal = _stage_balance(WORKLOADS[key].shape, batch)
+    bal, wins, ksplit = _stage_balance(WORKLOADS[key].shape, batch)
     for st in (GU, DOWN, LM):
-        assert bal[st] >= 0.97, (key, batch, st, bal)
+        assert bal[st] >= (0.93 if st in ksplit else 0.97), (key, batch, st, bal)
+    for st in ksplit:
+        assert wins[st] == 1, (key, batch, st, wins)
     assert min(bal.values()) >= 0.74, bal
