@@ -52,6 +52,9 @@ def parse():
                          "sequence scattered over the pool; no CPU or per-operation baselines)")
     ap.add_argument("--paged-order", choices=("permuted", "sequential"), default="permuted",
                     help="block ids of the paged pools: a seeded permutation, or each sequence's blocks in order")
+    ap.add_argument("--cold", action="store_true",
+                    help="rewrite a 2 GiB buffer before every timed step (outside its events) so that no "
+                         "weight or KV byte is served from the 256 MB memory-side cache or the L2s")
     ap.add_argument("--context-sweep", action="store_true",
                     help="Qwen3-8B-shaped model at batch 1 and 8 over contexts 64-4096, with and without "
                          "context routing (mk_set_context_bound); prints one JSON line and exits")
@@ -117,9 +120,12 @@ class Run:
         self.eng = DecodeEngine(self.shape, self.weights, max_batch=wl.batch_cap, max_seq=self.seq_cap)
         self.create_ms = (time.perf_counter() - t0) * 1e3
 
-    def phase(self, b, warmup, steps):
+    def phase(self, b, warmup, steps, scrub=None):
         """warmup + steps chained decode steps at batch b; per-step kernel time
-        from HIP events on the launch stream, wall time of the timed steps."""
+        from HIP events on the launch stream, wall time of the timed steps.
+        `scrub`: a device buffer rewritten before every timed step, outside its
+        events, so each step starts with cold caches (the wall time then
+        includes the scrubs)."""
         import torch
         from decode_megakernel_amd.bytes_model import step_bytes
         stream = torch.cuda.current_stream()
@@ -153,6 +159,8 @@ class Run:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(steps):
+            if scrub is not None:
+                scrub.add_(1)
             starts[k].record(stream)
             step(warmup + k)
             ends[k].record(stream)
@@ -436,9 +444,11 @@ def main():
     if args.paged:
         args.no_cpu_baseline = args.no_per_op = True
     run = Run(wl, n, args.paged, args.paged_order)
+    scrub = torch.zeros(1 << 29, dtype=torch.float32, device="cuda") if args.cold else None
     for p in wl.phases[:-1]:
         run.phase(p.batch, args.warmup, 1)
-    ph = run.phase(wl.phases[-1].batch, args.warmup, args.steps)
+    ph = run.phase(wl.phases[-1].batch, args.warmup, args.steps, scrub)
+    del scrub
     b = ph["batch"]
     head = summarize(ph)
     kernel_s = sum(ph["per_step_s"])
@@ -483,6 +493,7 @@ def main():
         "data": "synthetic: seeded random-init bf16 weights N(0,0.02), N(0,1) prompt KV, uniform first tokens",
         "config": {"workload": wl.key, "shape": wl.shape.name, "batch": b,
                    "kv_cache": f"paged, {args.paged}-position blocks, {args.paged_order}" if args.paged else "contiguous",
+                   "caches": "cold (2 GiB rewritten before every timed step)" if args.cold else "warm",
                    "context_at_first_timed_step": ph["context_at_first_timed_step"], "note": wl.note},
         "mbu": round(achieved / HBM_PEAK_BYTES_PER_S, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK_BYTES_PER_S / 1e9,

@@ -158,7 +158,7 @@ static PlanCfg plan_cfg(const mk_model_cfg* c, int ncu, int xb, int mfma_min) {
       if (f && (f == v || f[-1] == ',')) p.stage_mode[st] = atoi(f + strlen(key));
     }
   }
-  p.ksplit_min_windows = env_int("MK_KSPLIT_MIN_WINDOWS", 5);
+  p.ksplit_min_windows = env_int("MK_KSPLIT_MIN_WINDOWS", 4);
   return p;
 }
 

@@ -195,7 +195,7 @@ struct PlanCfg {
   int stage_mode[6] = {0, 0, 0, 0, 0, 0};  // per stage, overrides gemv_mode when non-zero; 3: stream-K, one-tile groups
   int attn_idle = 1;    // attention prefers the CUs its layer's QKV stage left idle
   int ksplit = 1;       // K-split stages whose tasks would need many LDS input windows
-  int ksplit_min_windows = 5;  // ... at least this many (per task of the tiling it replaces)
+  int ksplit_min_windows = 4;  // ... at least this many (per task of the tiling it replaces)
   int skip_prev = 2;    // row-owner stages skip the CUs of a previous stage that left CUs idle
                         // when the tiles per CU grow by at most skip_prev - 1 (0: never)
 };

@@ -125,7 +125,8 @@ Tiling tile_stage(const PlanCfg& p, int st, int M, int K, int tpw, int b) {
   // every CU; the pieces cost one 1 KB partial tile per (piece, sub-tile).
   // Worth it only when the tiling it replaces restages many windows per task
   // (measured: with 1-block windows at batch 16, 7-10 windows per task gained
-  // 13%; at batch 8-9, 2-3 windows of 2-3 blocks each lost 4-8%).
+  // 13% and the O projection's 4 gained 2%; at batch 8-9, 2-3 windows of 2-3
+  // blocks each lost 4-8%).
   const Tiling& rep = use_owner ? own : best;
   const long long rep_kbs = rep.owner ? nkb : std::min<long long>(nkb, (rep.ncols + p.ncu - 1) / p.ncu);
   const long long rep_windows = (rep_kbs + wkb - 1) / wkb;
