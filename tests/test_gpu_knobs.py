@@ -7,7 +7,9 @@ handle is created):
     on the VALU (batch 7) and MFMA (batch 9, 16) tiles;
   * MK_GEMV_MODE=1 forces row-owner tiling, =2 stream-K tiling, for every stage;
   * MK_MFMA_MIN_BATCH=4 runs batches 4-7 on the MFMA tiles;
-  * MK_KSPLIT=0 turns K-split off (Llama-2-13B-width model at batch 16).
+  * MK_KSPLIT=0 turns K-split off (Llama-2-13B-width model at batch 16);
+  * MK_KSPLIT_ALIGNED=0 deals K-split units evenly over the CUs instead of
+    piece by piece; MK_NUM_CU=2 runs on two CUs (fewer CUs than K pieces).
 The default choices are covered by the other parity tests."""
 import pytest
 
@@ -31,6 +33,10 @@ CASES = [
     ({"MK_MFMA_MIN_BATCH": "4"}, SMALL_LLAMA_H64, CTX7[:4]),
     ({"MK_MFMA_MIN_BATCH": "4"}, SMALL_MHA_H128, CTX7),
     ({"MK_KSPLIT": "0"}, SMALL_MHA_H128, CTX16),
+    # K-split units dealt evenly over the CUs (not piece by piece), and a
+    # 2-CU launch with fewer CUs than K pieces
+    ({"MK_KSPLIT_MIN_WINDOWS": "2", "MK_KSPLIT_ALIGNED": "0"}, SMALL_WIDE_FFN, CTX9),
+    ({"MK_KSPLIT_MIN_WINDOWS": "2", "MK_NUM_CU": "2"}, SMALL_WIDE_FFN, CTX9),
 ]
 
 

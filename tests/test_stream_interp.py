@@ -20,6 +20,10 @@ CASES = [
     (SMALL_WIDE_FFN, [9, 120, 31], 16, {"MK_KSPLIT_MIN_WINDOWS": "2"}),
     (SMALL_WIDE_FFN, [9, 120, 31, 4, 60, 2, 70, 11, 5], 32, {"MK_KSPLIT_MIN_WINDOWS": "2"}),
     (SMALL_LLAMA_H64, [300, 2, 45], 40, {"MK_GEMV_MODE": "2"}),
+    # fewer CUs than K pieces (down projection: 3 pieces on 2 CUs): units dealt evenly
+    (SMALL_WIDE_FFN, [9, 120, 31, 4, 60, 2, 70, 11, 5], 2, {"MK_KSPLIT_MIN_WINDOWS": "2"}),
+    # K-split units dealt evenly over the CUs instead of piece by piece
+    (SMALL_WIDE_FFN, [9, 120, 31, 4, 60, 2, 70, 11, 5], 13, {"MK_KSPLIT_MIN_WINDOWS": "2", "MK_KSPLIT_ALIGNED": "0"}),
 ]
 
 
