@@ -617,6 +617,14 @@ __device__ __forceinline__ bool next_piece(const Ctrl* c, int b, int nkv, int rp
 // so the lookup never waits behind the loader's streaming loads.
 template <bool UNIFORM>
 __device__ __forceinline__ int kv_block(DArgs A, int i, int lb) {
+  if constexpr (UNIFORM) {
+    // the index through readfirstlane, so the entry comes from a scalar
+    // load: a vector load here would make the loader wait for every DMA it
+    // has in flight (one vmcnt) before the next chunk (measured: 13B b16
+    // 17.9 -> 19.9 ms with one block per sequence)
+    i = __builtin_amdgcn_readfirstlane(i);
+    lb = __builtin_amdgcn_readfirstlane(lb);
+  }
   const size_t idx = (size_t)i * A->bt_stride + lb;
   int blk = UNIFORM ? __builtin_amdgcn_readfirstlane(as_const(A->btab)[idx]) : A->btab[idx];
   if ((unsigned)blk >= (unsigned)A->nblocks) {
@@ -628,6 +636,7 @@ __device__ __forceinline__ int kv_block(DArgs A, int i, int lb) {
 template <bool UNIFORM>
 __device__ __forceinline__ size_t kv_row(DArgs A, int l, int i, int g, int p) {
   if (A->btab) {
+    if constexpr (UNIFORM) p = __builtin_amdgcn_readfirstlane(p);
     const int lb = p / A->bsize;
     const int blk = kv_block<UNIFORM>(A, i, lb);
     return (((size_t)l * A->nblocks + blk) * A->nkv + g) * A->bsize + (p - lb * A->bsize);
@@ -864,7 +873,7 @@ __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
           // a paged chunk (at most 64 rows, blocks at least 64 positions)
           // spans at most two blocks, rows [0, split) in the first; one that
           // lies in a single block loads like a contiguous chunk
-          const int split = A->btab ? min(rows, (p0 / A->bsize + 1) * A->bsize - p0) : rows;
+          const int split = A->btab ? min(rows, (__builtin_amdgcn_readfirstlane(p0) / A->bsize + 1) * A->bsize - p0) : rows;
           if (split < rows) {
             const size_t r1 = kv_row<true>(A, t.layer, P.i, P.g, p0 + split) * A->hd;
             if (A->hd == 128)
