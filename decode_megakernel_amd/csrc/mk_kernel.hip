@@ -819,6 +819,8 @@ __device__ __forceinline__ void ring_issued(DArgs A, Ctrl* c, LoaderRing& R, int
 
 __device__ __noinline__ void loader_main(DArgs A, int cu, int lw, int lane) {
   A = uni(A);
+  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
+  lw = __builtin_amdgcn_readfirstlane(lw);
   char* ring = mk_lds;
   Ctrl* c = ctrl_block(A);
   const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
@@ -1403,6 +1405,8 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   constexpr int NV = NB > 0 ? NB : 1;
   constexpr int kResidTiles = 2;  // owned sub-tiles whose residual is prefetched
   A = uni(A);
+  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
+  w = __builtin_amdgcn_readfirstlane(w);
   char* ring = mk_lds;
   char* xb = xb_stage(A);
   float* red = red_scratch(A);
@@ -1823,6 +1827,8 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
 constexpr int kFinBatch = MK_FIN_BATCH;  // pieces polled per batch, every load in flight
 __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
+  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
+  w = __builtin_amdgcn_readfirstlane(w);
   Ctrl* c = ctrl_block(A);
   CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
@@ -1941,6 +1947,8 @@ __device__ __noinline__ bool fin_task(DArgs A, TaskP tp, int cu, int w, int lane
 //      RMSNorm's input and per-16-column sums of squares.
 __device__ __noinline__ bool embed_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   A = uni(A);
+  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
+  w = __builtin_amdgcn_readfirstlane(w);
   Ctrl* c = ctrl_block(A);
   CState& s = c->cs[w];
   const Task t = load_task(uni(tp));
@@ -2028,6 +2036,8 @@ template <int HD, int GM>
 __device__ __noinline__ bool attn_task(DArgs A, TaskP tp, int cu, int w, int lane) {
   static_assert(GM <= 8, "at most 8 query heads per KV head");
   A = uni(A);
+  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
+  w = __builtin_amdgcn_readfirstlane(w);
   char* ring = mk_lds;
   Ctrl* c = ctrl_block(A);
   CState& s = c->cs[w];
@@ -2766,6 +2776,8 @@ __device__ __forceinline__ bool gemv_dispatch(DArgs A, TaskP tp, int cu, int w, 
 
 __device__ __noinline__ void compute_main(DArgs A, int cu, int w, int lane) {
   A = uni(A);
+  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
+  w = __builtin_amdgcn_readfirstlane(w);
   Ctrl* c = ctrl_block(A);
   const TaskP T = as_const(A->tasks) + as_const(A->task_off)[cu];
   const int nt = as_const(A->task_off)[cu + 1] - as_const(A->task_off)[cu];
