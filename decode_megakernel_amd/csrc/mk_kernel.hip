@@ -1405,8 +1405,12 @@ __device__ __noinline__ bool gemv_task(DArgs A, TaskP tp, int cu, int w, int lan
   constexpr int NV = NB > 0 ? NB : 1;
   constexpr int kResidTiles = 2;  // owned sub-tiles whose residual is prefetched
   A = uni(A);
-  cu = __builtin_amdgcn_readfirstlane(cu);  // wave-uniform: scalar loads, no vmcnt drain
-  w = __builtin_amdgcn_readfirstlane(w);
+  if constexpr (NB == 0) {
+    // wave-uniform: scalar loads, no vmcnt drain (the VALU instantiations run
+    // slower with these in scalar registers: measured on the b1 models)
+    cu = __builtin_amdgcn_readfirstlane(cu);
+    w = __builtin_amdgcn_readfirstlane(w);
+  }
   char* ring = mk_lds;
   char* xb = xb_stage(A);
   float* red = red_scratch(A);
