@@ -9,7 +9,12 @@
   * Continuous batching: sequences leave and join between steps by rewriting
     block-table rows; each sequence is checked against its own oracle state.
   * A block-table entry outside the pool is clamped and raises
-    MK_STATUS_BAD_BLOCK (every access stays inside the pool)."""
+    MK_STATUS_BAD_BLOCK (every access stays inside the pool).
+  * At the benchmark's full sizes (Llama-3-8B b8 -> b9 and Llama-2-13B b16,
+    whose contiguous runs are compared with the oracle at every mid-state in
+    test_gpu_workloads), pools of 256-position blocks in seeded permuted
+    order give steps bit-identical to the contiguous cache, the ninth
+    sequence's join included."""
 import numpy as np
 import pytest
 import torch
@@ -17,8 +22,8 @@ import torch
 import oracle
 from decode_megakernel_amd.binding import DecodeEngine, STATUS_BAD_BLOCK
 from gpu_harness import log, rel_l2, TOL
-from mkinputs import (SMALL_QWEN_H128, SMALL_MHA_H128, SMALL_MHA_H64, SMALL_LLAMA_H64, make_weights, make_kv_cache,
-                      bf16_bits, draw_tokens, BF16_NAN_SENTINEL)
+from mkinputs import (SMALL_QWEN_H128, SMALL_MHA_H128, SMALL_MHA_H64, SMALL_LLAMA_H64, WORKLOADS, make_weights,
+                      make_kv_cache, make_paged_kv, bf16_bits, draw_tokens, draw_contexts, kv_capacity, BF16_NAN_SENTINEL)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +180,55 @@ def test_bad_block_is_clamped_and_reported():
         assert bool(torch.isfinite(logits[1]).all())
     finally:
         eng.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["llama3-8b-b8to9", "llama2-13b-b16"])
+def test_paged_full_size_matches_contiguous(key):
+    wl = WORKLOADS[key]
+    sh = wl.shape
+    steps = 2  # per phase
+    ctx = draw_contexts(wl.seed, wl.batch_cap, wl.ctx_lo, wl.ctx_hi)
+    cap = kv_capacity(max(ctx) + 1, steps * len(wl.phases))
+    log(f"case {key} paged 256 vs contiguous, contexts {ctx}, capacity {cap}")
+    w = make_weights(sh, wl.seed, device="cuda")
+    K, V = make_kv_cache(sh, wl.seed, ctx, wl.batch_cap, cap, device="cuda")
+    Kp, Vp, bt = make_paged_kv(sh, wl.seed, ctx, wl.batch_cap, cap, 256, device="cuda", permute=True)
+    e_c = DecodeEngine(sh, w, max_batch=wl.batch_cap, max_seq=cap)
+    e_p = DecodeEngine(sh, w, max_batch=wl.batch_cap, max_seq=cap)
+    toks = draw_tokens(wl.seed, wl.batch_cap, sh.vocab)
+    done = [0] * wl.batch_cap
+    try:
+        for ph in wl.phases:
+            b = ph.batch
+            for s in range(steps):
+                pos = [ctx[i] + done[i] for i in range(b)]
+                lc = torch.empty((b, sh.vocab), dtype=torch.float32, device="cuda")
+                lp = torch.empty_like(lc)
+                nc = torch.empty(b, dtype=torch.int32, device="cuda")
+                np_ = torch.empty_like(nc)
+                lens = [p + 1 for p in pos]
+                e_c.step(_ints(toks[:b]), _ints(pos), _ints(lens), K, V, lc, nc)
+                e_p.step_paged(_ints(toks[:b]), _ints(pos), _ints(lens), Kp, Vp, bt, lp, np_)
+                torch.cuda.synchronize()
+                assert e_c.status() == 0 and e_p.status() == 0
+                same = torch.equal(lc, lp) and torch.equal(nc, np_)
+                # this step's new rows: where the table puts them, equal to the contiguous cache's
+                rows_same = True
+                for i in range(b):
+                    blk, off = int(bt[i, pos[i] // 256]), pos[i] % 256
+                    rows_same = rows_same and torch.equal(Kp[:, blk, :, off].view(torch.int16),
+                                                          K[:, i, :, pos[i]].view(torch.int16))
+                    rows_same = rows_same and torch.equal(Vp[:, blk, :, off].view(torch.int16),
+                                                          V[:, i, :, pos[i]].view(torch.int16))
+                log(f"  {key} batch {b} step {s}: logits and tokens identical {same}, new rows identical {rows_same}")
+                assert same and rows_same
+                for i in range(b):
+                    done[i] += 1
+                toks[:b] = [int(t) for t in np_.cpu()]
+    finally:
+        e_c.close()
+        e_p.close()
+        del K, V, Kp, Vp, w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
